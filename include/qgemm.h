@@ -1,0 +1,152 @@
+/*
+ * qgemm — weight-quantized mixed-precision matrix product for AMD MI355X (gfx950).
+ *
+ *     C[M,N] = A[M,K] . dequant(Wq[K,N])
+ *
+ * Problem statement: BitBLAS issue #252 ("Default Backend Should be changed
+ * into tilelang ..."), reproduction script — a MatmulConfig is M, N, K,
+ * A_dtype, W_dtype, out_dtype, accum_dtype, layout "nt", with_bias,
+ * group_size, with_scaling, with_zeros, zeros_mode.  Parallel-k (k-parts)
+ * follows hidet issue #364 ("[Graph][Quantization] Multi-stage software
+ * pipelining and update parallel k rule"): K is split into parts whose
+ * partial products are reduced with atomics.  Affine dequantisation
+ * w = (q - z) * s follows torchao issue #2752 (AffineQuantizedTensor).
+ * int8 products accumulate into and return int32 (Triton PR #3595).
+ *
+ * Supported formats (a_dtype, w_dtype, out_dtype, accum_dtype):
+ *   W4A16 : (F16, I4 | U4, F16, F32)   per-group fp16 scales, optional zero points (U4)
+ *   dense : (F16, F16,     F16, F32)
+ *   W8A8  : (I8,  I8,      I32, I32)   exact
+ *   W2A8  : (I8,  I2,      I32, I32)   exact
+ * Any other tuple returns QGEMM_ERR_UNSUPPORTED (fp16 accumulation and int8
+ * output are not provided: the int8 narrowing rule is unspecified).
+ *
+ * Canonical input layout ("nt"; all row-major, little-endian):
+ *   A        [M, K]      fp16 or int8
+ *   W  I4/U4 uint32 [N, K/8]   value (k, n) in bits 4*(k%8) of word n*(K/8) + k/8
+ *      I2    uint32 [N, K/16]  value (k, n) in bits 2*(k%16) of word n*(K/16) + k/16
+ *      I8    int8   [N, K]     F16 fp16 [N, K]
+ *      signed values are two's complement of the field width; U4 is plain binary.
+ *   scales   fp16 [N, G], zeros fp16 [N, G]; G = K/g for g > 0, G = 1 for g = -1.
+ *   C        [M, N]      fp16 or int32
+ * Dequantised weight: w = q (g == 0), w = q*s (no zeros), w = (q - z)*s (zeros),
+ * with s, z taken at column n and group k / g.
+ *
+ * Packed weights: qgemm_pack_weights writes an opaque blob of packed_bytes
+ * (weights pre-shuffled into the MFMA operand order of gfx950, 1 KiB per
+ * 16-column x KB-row block, plus relaid scales and zeros).  The blob depends
+ * only on (N, K, w_dtype, group_size, has_zeros): plans that differ only in M,
+ * k_parts or flags can share one packed weight.
+ *
+ * Ownership and streams: every device buffer is allocated and owned by the
+ * caller; the library allocates no device memory.  A plan owns only host
+ * memory and is immutable after creation, so it may be used from several
+ * threads at once.  `stream` is a hipStream_t passed as void* (NULL = the
+ * null stream); every device call is asynchronous on it.  Concurrent
+ * qgemm_run calls on one plan need distinct workspaces and outputs.
+ *
+ * Errors: every call returns a status; nothing is thrown across the ABI.
+ * Argument errors are found before any device call (qgemm_create makes no
+ * HIP call at all).  A failed launch returns QGEMM_ERR_DEVICE.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct qgemm_plan qgemm_plan;
+
+typedef enum {
+  QGEMM_OK = 0,
+  QGEMM_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, bad flag, too-small buffer */
+  QGEMM_ERR_UNSUPPORTED = 2, /* legal request outside the supported formats or shapes */
+  QGEMM_ERR_NO_MEMORY = 3,   /* host allocation of the plan failed */
+  QGEMM_ERR_DEVICE = 4       /* a kernel launch failed */
+} qgemm_status;
+
+typedef enum {
+  QGEMM_F16 = 1,
+  QGEMM_F32 = 2,
+  QGEMM_I32 = 3,
+  QGEMM_I8 = 4,
+  QGEMM_I4 = 5, /* signed int4, [-8, 7] */
+  QGEMM_U4 = 6, /* unsigned int4, [0, 15] */
+  QGEMM_I2 = 7  /* signed int2, [-2, 1] */
+} qgemm_dtype;
+
+/* flags for qgemm_create */
+#define QGEMM_DETERMINISTIC 1u /* k_parts > 1: fixed-order two-pass reduction instead of atomics */
+
+/* execution path chosen by a plan (qgemm_plan_path) */
+#define QGEMM_PATH_GEMV 1 /* M <= 8: wavefront dot-product kernel, no matrix cores */
+#define QGEMM_PATH_MFMA 2 /* M > 8: LDS-staged MFMA tiles */
+
+/*
+ * Create a plan.  No device call.
+ *   M, N, K       problem sizes, each >= 1.  K must be a multiple of the block
+ *                 depth of the weight format: 128 (I4/U4), 256 (I2), 64 (I8),
+ *                 32 (F16), else QGEMM_ERR_UNSUPPORTED.
+ *   group_size    0 = no scaling (with_scaling False), -1 = one group per output
+ *                 column over all of K, g > 0 = groups of g along K.  Scaled
+ *                 formats are I4/U4 only; g > 0 must divide K and be a multiple
+ *                 of 32.  Other weight formats require 0.
+ *   has_zeros     0 or 1; 1 only with w_dtype U4 and group_size != 0.
+ *   k_parts       >= 1: number of contiguous, group-aligned K ranges computed by
+ *                 separate workgroups and reduced with fp32/int32 global atomics
+ *                 (or two-pass, QGEMM_DETERMINISTIC).  At most K / unit, where
+ *                 unit = max(block depth, group_size).
+ *   flags         0 or QGEMM_DETERMINISTIC.
+ *   packed_bytes  out: size of the packed blob for qgemm_pack_weights/qgemm_run.
+ *   workspace_bytes out: size of the device workspace qgemm_run needs (0 if none).
+ */
+qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K,
+                          qgemm_dtype a_dtype, qgemm_dtype w_dtype, qgemm_dtype out_dtype,
+                          qgemm_dtype accum_dtype, int32_t group_size, int32_t has_zeros,
+                          int32_t k_parts, uint32_t flags, size_t* packed_bytes,
+                          size_t* workspace_bytes);
+
+/*
+ * Pack canonical weights (device memory, layout above) into the plan's blob.
+ *   w       device, canonical weights.
+ *   scales  device, fp16 [N, G]; required iff group_size != 0, else ignored.
+ *   zeros   device, fp16 [N, G]; required iff has_zeros, else ignored.
+ *   packed  device, >= packed_bytes, 16-byte aligned; fully overwritten.
+ * Asynchronous on `stream`; run once per weight, outside the hot loop.
+ */
+qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const void* scales,
+                                const void* zeros, void* packed, void* stream);
+
+/*
+ * C = A . dequant(W) on `stream`.
+ *   A          device, [M, K] fp16 or int8, 16-byte aligned.
+ *   packed     device, the blob written by qgemm_pack_weights.
+ *   C          device, [M, N] fp16 or int32; fully overwritten.
+ *   workspace  device, >= workspace_bytes (may be NULL when that is 0),
+ *              16-byte aligned; scratch for split-K partials, its contents on
+ *              entry are ignored.
+ * Split-K with atomics sums in an unspecified order: fp16 results may differ
+ * in the last bits between runs; int32 results are exact.  With
+ * QGEMM_DETERMINISTIC the result is bitwise reproducible.
+ */
+qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed, void* C,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Release a plan; NULL is a no-op.  Device buffers are the caller's. */
+void qgemm_destroy(qgemm_plan* plan);
+
+/* Path the plan chose (QGEMM_PATH_GEMV or QGEMM_PATH_MFMA), or -1 for NULL. */
+int32_t qgemm_plan_path(const qgemm_plan* plan);
+
+/* Short static description of a status code. */
+const char* qgemm_status_string(qgemm_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

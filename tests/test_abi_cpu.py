@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI (no device calls): the library loads, exports
+every function the header declares, and qgemm_create / qgemm_pack_weights /
+qgemm_run reject bad arguments with the documented status before any launch.
+"""
+import os
+import re
+
+import pytest
+
+from weight_quantized_mixed_amd import qgemm as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "bitblas_matmul_grid.txt")
+
+
+def test_library_exports_every_declared_function():
+    lib = q.load()
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(qgemm_[a-z_]+)\s*\(", text, re.M))
+    assert declared == set(q.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _create(**kw):
+    args = dict(M=1, N=4096, K=4096, a_dtype="f16", w_dtype="i4", out_dtype="f16", accum_dtype="f32",
+                group_size=128, has_zeros=0, k_parts=1, flags=0)
+    args.update(kw)
+    return q.qgemm_create(**args)
+
+
+def _status(**kw):
+    try:
+        plan, _, _ = _create(**kw)
+    except q.QGemmError as e:
+        return e.status
+    q.qgemm_destroy(plan)
+    return q.QGEMM_OK
+
+
+def test_create_valid_formats():
+    for kw in [dict(), dict(w_dtype="u4", has_zeros=1), dict(w_dtype="f16", group_size=0),
+               dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0),
+               dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=0)]:
+        assert _status(**kw) == q.QGEMM_OK, kw
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), q.QGEMM_ERR_INVALID_ARG),
+    (dict(N=-3), q.QGEMM_ERR_INVALID_ARG),
+    (dict(K=0), q.QGEMM_ERR_INVALID_ARG),
+    (dict(k_parts=0), q.QGEMM_ERR_INVALID_ARG),
+    (dict(k_parts=33), q.QGEMM_ERR_INVALID_ARG),          # 4096 / 128 = 32 units
+    (dict(flags=2), q.QGEMM_ERR_INVALID_ARG),
+    (dict(has_zeros=2), q.QGEMM_ERR_INVALID_ARG),
+    (dict(group_size=-2), q.QGEMM_ERR_INVALID_ARG),
+    (dict(a_dtype=99), q.QGEMM_ERR_INVALID_ARG),
+    (dict(accum_dtype="f16"), q.QGEMM_ERR_UNSUPPORTED),   # fp16 accumulation
+    (dict(a_dtype="i8", w_dtype="i8", out_dtype="i8", accum_dtype="i32", group_size=0),
+     q.QGEMM_ERR_UNSUPPORTED),                              # int8 output
+    (dict(w_dtype="i8"), q.QGEMM_ERR_UNSUPPORTED),          # fp16 x int8
+    (dict(has_zeros=1), q.QGEMM_ERR_UNSUPPORTED),           # zeros need uint4
+    (dict(w_dtype="u4", has_zeros=1, group_size=0), q.QGEMM_ERR_UNSUPPORTED),
+    (dict(group_size=48), q.QGEMM_ERR_UNSUPPORTED),         # not a multiple of 32
+    (dict(group_size=96, K=4096), q.QGEMM_ERR_UNSUPPORTED),  # does not divide K
+    (dict(K=4000), q.QGEMM_ERR_UNSUPPORTED),                # not a multiple of 128
+    (dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=0, K=4224),
+     q.QGEMM_ERR_UNSUPPORTED),                              # int2 blocks are 256 deep
+    (dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=128),
+     q.QGEMM_ERR_UNSUPPORTED),                              # int formats are unscaled
+])
+def test_create_rejects(kw, status):
+    assert _status(**kw) == status
+
+
+def test_sizes_and_paths():
+    plan, pb, wb = _create()
+    assert pb == 4096 * 4096 // 2 + 4096 * 32 * 2 and wb == 0
+    assert q.qgemm_plan_path(plan) == q.QGEMM_PATH_GEMV
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(M=9, N=100, k_parts=4)
+    npad = 256
+    assert pb == npad * 4096 // 2 + npad * 32 * 2
+    assert wb == 9 * 100 * 4                                # fp32 atomic accumulator
+    assert q.qgemm_plan_path(plan) == q.QGEMM_PATH_MFMA
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(M=9, N=100, k_parts=4, flags=q.QGEMM_DETERMINISTIC)
+    assert wb == 4 * 9 * 100 * 4                            # per-part partials
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32",
+                           group_size=0, k_parts=4)
+    assert wb == 0                                          # int32 atomics go straight into C
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(w_dtype="u4", has_zeros=1, N=4096)
+    assert pb == 4096 * 4096 // 2 + 32 * 4096 * 4           # (scale, zero) pairs
+    q.qgemm_destroy(plan)
+
+
+def test_null_and_misaligned_arguments_rejected_before_launch():
+    plan, pb, wb = _create(k_parts=2, flags=q.QGEMM_DETERMINISTIC)
+    try:
+        for args in [(0, 16, 16, 16), (16, 0, 16, 16), (16, 16, 0, 16), (16, 16, 16, 0)]:
+            with pytest.raises(q.QGemmError) as e:
+                q.qgemm_run(plan, args[0], args[1], args[2], args[3], wb, 0)
+            assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_run(plan, 16, 16, 16, 16, wb - 1, 0)       # workspace too small
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_run(plan, 18, 16, 16, 16, wb, 0)           # A not 16-byte aligned
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_pack_weights(plan, 16, 0, 0, 16, 0)        # scales missing
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_pack_weights(plan, 16, 16, 0, 0, 0)        # no output
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+    finally:
+        q.qgemm_destroy(plan)
+    assert q.qgemm_plan_path(0) == -1
+    q.qgemm_destroy(0)                                         # NULL is a no-op
+    assert q.qgemm_status_string(2) == "unsupported format or shape"
+
+
+# the pages' benchmark grid: config strings of the BitBLAS issue #252 tables
+_FIELDS = ["M", "N", "K", "A_dtype", "W_dtype", "out_dtype", "accum_dtype", "layout", "with_bias",
+           "group_size", "with_scaling", "with_zeros", "zeros_mode"]
+_DT = {"float16": "f16", "int8": "i8", "int4": "i4", "int2": "i2", "int32": "i32"}
+
+
+def _parse(line):
+    # "1-16384-16384-float16-int4-float16-float16-nt-False--1-True-False-None": the group size
+    # -1 shows up as an empty field followed by "1"
+    parts = line.split("-")
+    if parts[9] == "" and parts[10] == "1":
+        parts = parts[:9] + ["-1"] + parts[11:]
+    assert len(parts) == 13, line
+    return dict(zip(_FIELDS, parts))
+
+
+def golden_grid():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            rows.append(_parse(line))
+    return rows
+
+
+def plan_args(cfg):
+    """Map one of the pages' configs to qgemm_create arguments.
+
+    fp16 accumulation becomes fp32 and int8 output becomes int32 (this library
+    returns the int32 accumulator); with_scaling False means group_size 0.
+    """
+    a, w = _DT[cfg["A_dtype"]], _DT[cfg["W_dtype"]]
+    out, acc = ("f16", "f32") if a == "f16" else ("i32", "i32")
+    g = int(cfg["group_size"]) if (w in ("i4", "u4") and cfg["with_scaling"] == "True") else 0
+    return dict(M=int(cfg["M"]), N=int(cfg["N"]), K=int(cfg["K"]), a_dtype=a, w_dtype=w,
+                out_dtype=out, accum_dtype=acc, group_size=g,
+                has_zeros=int(cfg["with_zeros"] == "True"), k_parts=1, flags=0)
+
+
+def test_pages_grid_maps_to_plans():
+    grid = golden_grid()
+    assert len(grid) == 25
+    assert {(c["M"]) for c in grid} == {"1", "32", "128", "512", "16384"}
+    for cfg in grid:
+        assert cfg["layout"] == "nt" and cfg["with_bias"] == "False"
+        args = plan_args(cfg)
+        plan, pb, wb = q.qgemm_create(**args)
+        want = q.QGEMM_PATH_GEMV if args["M"] <= 8 else q.QGEMM_PATH_MFMA
+        assert q.qgemm_plan_path(plan) == want
+        q.qgemm_destroy(plan)

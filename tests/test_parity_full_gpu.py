@@ -1,0 +1,87 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration the
+benchmark times, on sampled outputs the oracle computes directly.
+
+Workloads: the pages' grid N = K = 16384 with M in {1, 32, 128, 512, 16384}
+(BitBLAS issue #252, reproduction script), the LLaMA-7B projection shapes of
+hidet issue #364 with k-parts 1 and 4, and W4A16 with g = 128.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import Case, assert_matches, say
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _sample(n, k, rng):
+    """k sorted distinct indices in [0, n), always including the first and last."""
+    idx = set(rng.choice(n, size=min(k, n), replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(idx))
+
+
+def _check_sampled(c, rows, cols, what):
+    gpu = c.run()
+    ref = c.reference(rows=rows, cols=cols)
+    assert_matches(gpu[np.ix_(rows, cols)], ref, what)
+    return gpu
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (1, 4096, 11008), (1, 11008, 4096),
+                                   (1, 4096, 32000), (128, 4096, 11008), (128, 11008, 4096),
+                                   (128, 4096, 4096), (128, 4096, 32000)])
+@pytest.mark.parametrize("kp", [1, 4])
+def test_w4a16_llama_shapes(M, K, N, kp):
+    say(f"W4A16 M={M} K={K} N={N} kp={kp}")
+    c = Case(M, N, K, "i4", 128, k_parts=kp, seed=synth.seed_for(1, M + kp))
+    rng = np.random.default_rng(0)
+    rows = np.arange(M) if M <= 8 else _sample(M, 24, rng)
+    cols = _sample(N, 512, rng)
+    _check_sampled(c, rows, cols, f"W4A16 {M}x{K}x{N} kp={kp}")
+
+
+@pytest.mark.parametrize("M", [1, 32, 128, 512])
+@pytest.mark.parametrize("w_dtype,kp", [("i8", 1), ("i8", 4), ("i2", 1), ("i2", 4)])
+def test_int_grid_full(M, w_dtype, kp):
+    say(f"{w_dtype} M={M} N=K=16384 kp={kp}")
+    c = Case(M, 16384, 16384, w_dtype, 0, k_parts=kp, seed=synth.seed_for(2 if w_dtype == "i8" else 3, M))
+    rng = np.random.default_rng(1)
+    rows = np.arange(M) if M <= 32 else _sample(M, 32, rng)
+    cols = _sample(16384, 384, rng)
+    _check_sampled(c, rows, cols, f"{w_dtype} M={M}")
+
+
+@pytest.mark.parametrize("kp", [1, 4])
+def test_w4a16_m1_16384(kp):
+    c = Case(1, 16384, 16384, "i4", 128, k_parts=kp, seed=synth.seed_for(5, kp))
+    gpu = c.run()
+    assert_matches(gpu, c.reference(), f"W4A16 M=1 16384 kp={kp}")
+
+
+def _tile_samples(rng, n_tiles=64, T=128, grid=128):
+    coords = {(0, 0), (0, grid - 1), (grid - 1, 0), (grid - 1, grid - 1)}
+    while len(coords) < n_tiles:
+        coords.add(tuple(rng.integers(0, grid, size=2).tolist()))
+    return sorted(coords)
+
+
+@pytest.mark.parametrize("variant", ["dense_f16", "u4_zeros_g128"])
+def test_large_m_sampled_tiles(variant):
+    """M = N = K = 16384 on 64 sampled 128 x 128 output tiles (incl. the 4 corners)."""
+    M = N = K = 16384
+    if variant == "dense_f16":
+        c = Case(M, N, K, "f16", 0, seed=synth.seed_for(4, 0))
+    else:
+        c = Case(M, N, K, "u4", 128, True, seed=synth.seed_for(4, 1))
+    say(f"large-M {variant}: path {c.q.path}")
+    gpu = c.run()
+    rng = np.random.default_rng(4)
+    for (ti, tj) in _tile_samples(rng):
+        rows = np.arange(ti * 128, ti * 128 + 128)
+        cols = np.arange(tj * 128, tj * 128 + 128)
+        ref = c.reference(rows=rows, cols=cols)
+        assert_matches(gpu[np.ix_(rows, cols)], ref, f"{variant} tile ({ti},{tj})")

@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer formats must match bit for bit; fp16 outputs within
+|gpu - ref| <= 1e-2 + 5e-3*|ref| of the unrounded float64 reference.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import Case, assert_matches, say
+from weight_quantized_mixed_amd import qgemm as q
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+# ---------------------------------------------------------------- small shapes, every path
+SMALL = [
+    # M, N, K, w_dtype, g, zeros
+    (1, 72, 512, "i4", 128, False),
+    (3, 300, 1024, "i4", 128, False),
+    (8, 136, 768, "i4", 64, False),
+    (2, 200, 512, "i4", 32, False),
+    (1, 264, 1024, "i4", -1, False),
+    (5, 88, 512, "i4", 0, False),
+    (4, 136, 1024, "u4", 128, True),
+    (1, 72, 512, "u4", 32, True),
+    (6, 100, 1024, "u4", 256, False),
+    (1, 200, 1024, "f16", 0, False),
+    (7, 72, 512, "f16", 0, False),
+    (1, 300, 1024, "i8", 0, False),
+    (8, 136, 512, "i8", 0, False),
+    (1, 200, 2048, "i2", 0, False),
+    (5, 72, 1024, "i2", 0, False),
+    # MFMA path (M > 8): several tiles and ragged tails in M and N
+    (9, 72, 512, "i4", 128, False),
+    (33, 200, 1024, "i4", 128, False),
+    (130, 264, 768, "i4", 64, False),
+    (129, 136, 512, "u4", 128, True),
+    (64, 72, 1024, "u4", 32, True),
+    (40, 88, 512, "i4", 0, False),
+    (70, 136, 512, "i4", -1, False),
+    (33, 200, 512, "f16", 0, False),
+    (257, 300, 256, "f16", 0, False),
+    (33, 300, 1024, "i8", 0, False),
+    (129, 136, 512, "i8", 0, False),
+    (9, 72, 2048, "i2", 0, False),
+    (160, 264, 1024, "i2", 0, False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,w_dtype,g,zeros", SMALL)
+@pytest.mark.parametrize("kp,det", [(1, False), (3, False), (3, True)])
+def test_small_parity(M, N, K, w_dtype, g, zeros, kp, det):
+    say(f"case M={M} N={N} K={K} {w_dtype} g={g} zeros={zeros} kp={kp} det={det}")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=M * 1000 + N + K)
+    assert c.q.path == (q.QGEMM_PATH_GEMV if M <= 8 else q.QGEMM_PATH_MFMA)
+    assert_matches(c.run(), c.reference(), f"M={M} N={N} K={K} {w_dtype} kp={kp}")
+
+
+# ---------------------------------------------------------------- layout pins (one-hot A)
+@pytest.mark.parametrize("M,w_dtype", [(1, "i4"), (20, "i4"), (1, "i2"), (40, "i2"), (1, "i8"), (40, "i8"),
+                                       (1, "f16"), (40, "f16")])
+def test_one_hot_activation_bitwise(M, w_dtype):
+    """A = e_k0 in every row: C[:, n] is the single dequantised weight, rounded once."""
+    N, K = 72, 512
+    base = synth.make_problem(M, N, K, w_dtype, group_size=128, seed=77)
+    for k0 in (0, 37, 128, 300, 511):
+        A = np.zeros((M, K), dtype=base.A.dtype)
+        A[:, k0] = 1
+        p = synth.make_problem(M, N, K, w_dtype, group_size=128, q=base.q, A=A, s=base.s, seed=77)
+        say(f"one-hot M={M} {w_dtype} k0={k0}")
+        c = Case(0, 0, 0, None, problem=p)
+        gpu = c.run()
+        ref = c.reference()
+        if ref.dtype == np.int64:
+            assert np.array_equal(gpu.astype(np.int64), ref)
+        else:
+            assert np.array_equal(gpu, oracle.round_fp16(ref)), k0
+
+
+def test_constant_closed_form_zeros():
+    """A = 1, q = c, zero point z, scale s0: C = K (c - z) s0 everywhere (MFMA and GEMV)."""
+    for M in (1, 24):
+        N, K, c0 = 80, 1024, 11
+        A = np.ones((M, K), dtype=np.float16)
+        qv = np.full((N, K), c0, dtype=np.int8)
+        s = np.full((N, K // 128), 0.0125, dtype=np.float16)
+        z = np.full((N, K // 128), 7.5, dtype=np.float16)
+        p = synth.make_problem(M, N, K, "u4", 128, True, q=qv, A=A, s=s, z=z)
+        gpu = Case(0, 0, 0, None, problem=p).run()
+        expect = K * (c0 - 7.5) * float(np.float16(0.0125))
+        assert np.all(gpu == np.float16(expect)), (M, gpu[0, :4], expect)
+
+
+# ---------------------------------------------------------------- split-K properties
+@pytest.mark.parametrize("M,w_dtype,g", [(1, "i4", 128), (4, "i8", 0), (64, "i4", 128), (33, "i2", 0)])
+def test_two_pass_is_bitwise_reproducible(M, w_dtype, g):
+    c = Case(M, 264, 2048, w_dtype, g, k_parts=4, deterministic=True, seed=5)
+    first = c.run()
+    for _ in range(9):
+        assert np.array_equal(c.run(), first)
+    assert_matches(first, c.reference(), "two-pass")
+
+
+@pytest.mark.parametrize("M,w_dtype", [(1, "i8"), (2, "i2"), (100, "i8"), (40, "i2")])
+def test_int_atomics_exact_every_run(M, w_dtype):
+    c = Case(M, 200, 4096, w_dtype, 0, k_parts=4, seed=6)
+    ref = c.reference()
+    for _ in range(3):
+        assert np.array_equal(c.run().astype(np.int64), ref)
+
+
+def test_kparts_agree_on_int():
+    p = synth.make_problem(3, 136, 4096, "i2", seed=9)
+    outs = [Case(0, 0, 0, None, k_parts=kp, problem=p).run() for kp in (1, 2, 4, 16)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+# ---------------------------------------------------------------- host-side errors on a live device
+def test_run_rejects_small_workspace():
+    c = Case(2, 72, 512, "i4", 128, k_parts=2, deterministic=True, seed=3)
+    ws = torch.empty(c.q.ws_bytes - 4, dtype=torch.uint8, device="cuda")
+    C = c.q.new_output()
+    with pytest.raises(q.QGemmError) as e:
+        q.qgemm_run(c.q.plan, c.A.data_ptr(), c.packed.data_ptr(), C.data_ptr(), ws.data_ptr(),
+                    ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+
+
+def test_shared_blob_across_plans():
+    """One packed weight serves the GEMV and the MFMA plan of the same (N, K, format)."""
+    N, K = 136, 1024
+    p1 = synth.make_problem(1, N, K, "i4", 128, seed=12)
+    c1 = Case(0, 0, 0, None, problem=p1)
+    p2 = synth.make_problem(48, N, K, "i4", 128, q=p1.q, s=p1.s, seed=13)
+    c2 = Case(0, 0, 0, None, problem=p2)
+    assert c1.q.packed_bytes == c2.q.packed_bytes
+    out = c2.q.run(c2.A, c1.packed)
+    torch.cuda.synchronize()
+    assert_matches(out.cpu().numpy(), c2.reference(), "shared blob")

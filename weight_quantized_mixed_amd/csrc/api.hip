@@ -1,0 +1,216 @@
+// Host side of the C ABI: argument validation, the packed-blob layout, path and
+// tile selection, and the launch sequence of one qgemm_run.
+//
+// The arguments follow the problem statement of BitBLAS issue #252
+// (reproduction script: M, N, K, A_dtype, W_dtype, out_dtype, accum_dtype,
+// group_size, with_scaling, with_zeros) plus hidet issue #364's k-parts.
+#include <new>
+
+#include "qgemm_internal.hpp"
+
+using namespace qg;
+
+struct qgemm_plan {
+  int64_t M, N, K;
+  qgemm_dtype a_dtype, w_dtype, out_dtype, accum_dtype;
+  int32_t group_size, has_zeros, k_parts;
+  uint32_t flags;
+  Layout L;
+  int path;          // QGEMM_PATH_GEMV or QGEMM_PATH_MFMA
+  int tile;          // MFMA tile
+  int gemv_waves;    // GEMV waves per workgroup
+  int32_t unit_kb, n_units;
+  size_t ws_bytes;
+};
+
+namespace {
+
+int fmt_of(qgemm_dtype w) {
+  switch (w) {
+    case QGEMM_I4: return FMT_I4;
+    case QGEMM_U4: return FMT_U4;
+    case QGEMM_F16: return FMT_F16;
+    case QGEMM_I8: return FMT_I8;
+    case QGEMM_I2: return FMT_I2;
+    default: return -1;
+  }
+}
+
+bool known_dtype(int d) { return d >= QGEMM_F16 && d <= QGEMM_I2; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bool zeros) {
+  L->fmt = fmt;
+  L->N = N;
+  L->K = K;
+  L->Npad = round_up(N, 256);
+  L->NB = L->Npad / 16;
+  L->nkb = K / kb_of(fmt);
+  L->group_size = g;
+  L->G = g == 0 ? 0 : g < 0 ? 1 : K / g;
+  L->zeros = zeros;
+  L->w_bytes = (size_t)L->nkb * (size_t)L->NB * 1024;
+  L->s_offset = (size_t)round_up((int64_t)L->w_bytes, 256);
+  L->s_bytes = (size_t)L->G * (size_t)L->Npad * (zeros ? 4 : 2);
+  L->total = L->s_offset + L->s_bytes;
+  return QGEMM_OK;
+}
+
+int choose_gemv_waves(const qgemm_plan* p) {
+  const int64_t rb = (p->N + 63) / 64;
+  const int64_t per_part = p->L.nkb / p->k_parts;
+  int64_t want = (2048 + rb * p->k_parts - 1) / (rb * p->k_parts);
+  int64_t maxw = per_part / 2;
+  if (maxw < 1) maxw = 1;
+  if (maxw > 16) maxw = 16;
+  if (want > maxw) want = maxw;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+int choose_tile(const qgemm_plan* p) {
+  if (p->M <= 32) return TILE_32x64;
+  const int64_t big = ((p->M + 127) / 128) * ((p->N + 127) / 128) * p->k_parts;
+  return big >= 256 ? TILE_128x128 : TILE_64x64;
+}
+
+RunArgs make_args(const qgemm_plan* p, const void* A, const void* packed, void* C, void* ws) {
+  RunArgs a;
+  a.A = A;
+  a.W = static_cast<const uint4*>(packed);
+  a.S = p->L.G ? static_cast<const char*>(packed) + p->L.s_offset : nullptr;
+  a.C = C;
+  a.ws = ws;
+  a.M = (int32_t)p->M;
+  a.N = (int32_t)p->N;
+  a.K = (int32_t)p->K;
+  a.Npad = (int32_t)p->L.Npad;
+  a.NB = (int32_t)p->L.NB;
+  a.nkb = (int32_t)p->L.nkb;
+  a.group_size = p->group_size;
+  const int KB = kb_of(p->L.fmt);
+  a.smode = p->group_size == 0 ? SC_NONE : (p->group_size > 0 && p->group_size < KB) ? SC_PIECE : SC_BLOCK;
+  a.zeros = p->has_zeros;
+  a.k_parts = p->k_parts;
+  a.unit_kb = p->unit_kb;
+  a.n_units = p->n_units;
+  a.waves = p->gemv_waves;
+  a.out_mode = p->k_parts == 1 ? OUT_STORE : (p->flags & QGEMM_DETERMINISTIC) ? OUT_PARTIAL : OUT_ATOMIC;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qgemm_dtype a_dtype,
+                          qgemm_dtype w_dtype, qgemm_dtype out_dtype, qgemm_dtype accum_dtype,
+                          int32_t group_size, int32_t has_zeros, int32_t k_parts, uint32_t flags,
+                          size_t* packed_bytes, size_t* workspace_bytes) {
+  if (!out) return QGEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (M < 1 || N < 1 || K < 1) return QGEMM_ERR_INVALID_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return QGEMM_ERR_UNSUPPORTED;
+  if (!known_dtype(a_dtype) || !known_dtype(w_dtype) || !known_dtype(out_dtype) || !known_dtype(accum_dtype))
+    return QGEMM_ERR_INVALID_ARG;
+  if (has_zeros != 0 && has_zeros != 1) return QGEMM_ERR_INVALID_ARG;
+  if (k_parts < 1) return QGEMM_ERR_INVALID_ARG;
+  if (flags & ~QGEMM_DETERMINISTIC) return QGEMM_ERR_INVALID_ARG;
+  if (group_size < -1) return QGEMM_ERR_INVALID_ARG;
+
+  // legal format tuples
+  const bool fp_tuple = a_dtype == QGEMM_F16 && out_dtype == QGEMM_F16 && accum_dtype == QGEMM_F32 &&
+                        (w_dtype == QGEMM_I4 || w_dtype == QGEMM_U4 || w_dtype == QGEMM_F16);
+  const bool int_tuple = a_dtype == QGEMM_I8 && out_dtype == QGEMM_I32 && accum_dtype == QGEMM_I32 &&
+                         (w_dtype == QGEMM_I8 || w_dtype == QGEMM_I2);
+  if (!fp_tuple && !int_tuple) return QGEMM_ERR_UNSUPPORTED;
+  const int fmt = fmt_of(w_dtype);
+  const int KB = kb_of(fmt);
+  const bool scaled_fmt = fmt == FMT_I4 || fmt == FMT_U4;
+
+  // scaling and zero points
+  if (!scaled_fmt && group_size != 0) return QGEMM_ERR_UNSUPPORTED;
+  if (has_zeros && (fmt != FMT_U4 || group_size == 0)) return QGEMM_ERR_UNSUPPORTED;
+  if (group_size > 0 && (K % group_size != 0 || group_size % 32 != 0)) return QGEMM_ERR_UNSUPPORTED;
+  if (K % KB != 0) return QGEMM_ERR_UNSUPPORTED;
+
+  const int64_t unit = group_size > KB ? group_size : KB;
+  const int64_t n_units = K / unit;
+  if (k_parts > n_units) return QGEMM_ERR_INVALID_ARG;
+
+  qgemm_plan* p = new (std::nothrow) qgemm_plan();
+  if (!p) return QGEMM_ERR_NO_MEMORY;
+  p->M = M;
+  p->N = N;
+  p->K = K;
+  p->a_dtype = a_dtype;
+  p->w_dtype = w_dtype;
+  p->out_dtype = out_dtype;
+  p->accum_dtype = accum_dtype;
+  p->group_size = group_size;
+  p->has_zeros = has_zeros;
+  p->k_parts = k_parts;
+  p->flags = flags;
+  fill_layout(&p->L, fmt, N, K, group_size, has_zeros != 0);
+  p->unit_kb = (int32_t)(unit / KB);
+  p->n_units = (int32_t)n_units;
+  p->path = M <= 8 ? QGEMM_PATH_GEMV : QGEMM_PATH_MFMA;
+  p->tile = choose_tile(p);
+  p->gemv_waves = choose_gemv_waves(p);
+  const size_t mn4 = (size_t)M * (size_t)N * 4;
+  if (k_parts == 1) p->ws_bytes = 0;
+  else if (flags & QGEMM_DETERMINISTIC) p->ws_bytes = mn4 * (size_t)k_parts;
+  else p->ws_bytes = out_dtype == QGEMM_F16 ? mn4 : 0;
+  if (packed_bytes) *packed_bytes = p->L.total;
+  if (workspace_bytes) *workspace_bytes = p->ws_bytes;
+  *out = p;
+  return QGEMM_OK;
+}
+
+qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const void* scales, const void* zeros,
+                                void* packed, void* stream) {
+  if (!plan || !w || !packed) return QGEMM_ERR_INVALID_ARG;
+  if (plan->L.G && !scales) return QGEMM_ERR_INVALID_ARG;
+  if (plan->L.zeros && !zeros) return QGEMM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(packed)) & 15) return QGEMM_ERR_INVALID_ARG;
+  hipError_t e = launch_pack(plan->L, w, scales, zeros, packed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_DEVICE;
+}
+
+qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed, void* C, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!plan || !A || !packed || !C) return QGEMM_ERR_INVALID_ARG;
+  if (plan->ws_bytes && (!workspace || workspace_bytes < plan->ws_bytes)) return QGEMM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(packed) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return QGEMM_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  RunArgs a = make_args(plan, A, packed, C, workspace);
+  const bool out_f16 = plan->out_dtype == QGEMM_F16;
+  hipError_t e = hipSuccess;
+  if (a.out_mode == OUT_ATOMIC)
+    e = launch_fill_zero(out_f16 ? workspace : C, (size_t)plan->M * plan->N * 4, st);
+  if (e == hipSuccess)
+    e = plan->path == QGEMM_PATH_GEMV ? launch_gemv(plan->L.fmt, a, st) : launch_mfma(plan->L.fmt, plan->tile, a, st);
+  if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))
+    e = launch_finalize(a, out_f16, st);
+  return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_DEVICE;
+}
+
+void qgemm_destroy(qgemm_plan* plan) { delete plan; }
+
+int32_t qgemm_plan_path(const qgemm_plan* plan) { return plan ? plan->path : -1; }
+
+const char* qgemm_status_string(qgemm_status s) {
+  switch (s) {
+    case QGEMM_OK: return "ok";
+    case QGEMM_ERR_INVALID_ARG: return "invalid argument";
+    case QGEMM_ERR_UNSUPPORTED: return "unsupported format or shape";
+    case QGEMM_ERR_NO_MEMORY: return "out of host memory";
+    case QGEMM_ERR_DEVICE: return "device launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal definitions shared by the host ABI and the kernels of libqgemm.
+//
+// Packed blob layout (written by the pack kernel, read by every compute kernel)
+// ---------------------------------------------------------------------------
+// Columns are padded to Npad = roundup(N, 256).  The weight region is a grid of
+// 1 KiB "superblocks", each 16 columns x KB reduction positions:
+//     superblock (nb, kb) at byte ((kb * (Npad/16)) + nb) * 1024
+// KB = 128 (int4), 256 (int2), 64 (int8), 32 (fp16): 16 bytes per column per
+// quarter of the block.  Inside a superblock, the 16-byte "piece" of column
+// nn = n % 16 and quarter kq sits at byte (kq*16 + nn) * 16, so one wave-wide
+// 16-byte load (lane l -> piece l) fetches the whole block in the lane order of
+// a gfx950 16x16 MFMA B operand (lane l: column l%16, K slice l/16).  A piece
+// covers the KB/4 consecutive positions kb*KB + kq*KB/4 + [0, KB/4):
+//   int4  4 words x 8 values; word t holds positions 8t..8t+7 with nibble
+//         slots (0..7) <- positions (0,2,4,6,1,3,5,7), stored offset-binary
+//         (q + 8 for signed, q for unsigned), so (w >> 4j) & 0x000F000F,
+//         or-ed with 0x6400 per half, is the fp16 pair (1024 + s[2j], 1024 + s[2j+1]).
+//   int2  4 words x 16 values; word t holds positions 16t..16t+15, value e in
+//         byte e%4 at bit 2*(e/4), stored offset-binary q + 2, so
+//         (w >> 2j) & 0x03030303 gives the four consecutive positions 4j..4j+3.
+//   int8  16 bytes = 16 consecutive positions.
+//   fp16  8 halves = 8 consecutive positions.
+// After the weights (256-byte aligned) come the scales as [G][Npad] fp16, or
+// (scale, zero) half pairs as [G][Npad] when zero points are present.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qgemm.h"
+
+namespace qg {
+
+enum Fmt : int { FMT_I4 = 0, FMT_U4 = 1, FMT_F16 = 2, FMT_I8 = 3, FMT_I2 = 4 };
+
+// output modes of a compute kernel
+enum OutMode : int {
+  OUT_STORE = 0,    // write C directly (k_parts == 1)
+  OUT_ATOMIC = 1,   // atomic add into fp32 workspace (fp16 out) or into C (int32 out)
+  OUT_PARTIAL = 2   // write the part's partial to workspace[part][M][N] (two-pass)
+};
+
+// scale modes
+enum ScaleMode : int {
+  SC_NONE = 0,   // group_size == 0
+  SC_BLOCK = 1,  // one group per superblock (g >= KB or g == -1)
+  SC_PIECE = 2   // one group per 32-position piece (g in {32, 64} for int4)
+};
+
+constexpr int kb_of(int fmt) {
+  return fmt == FMT_I2 ? 256 : fmt == FMT_I8 ? 64 : fmt == FMT_F16 ? 32 : 128;
+}
+
+struct Layout {
+  int fmt;
+  int64_t N, K, Npad, NB, nkb;
+  int32_t group_size;  // as given: 0, -1 or g > 0
+  int64_t G;           // number of scale groups (0 without scaling)
+  bool zeros;
+  size_t w_bytes, s_offset, s_bytes, total;
+};
+
+// Arguments of every compute kernel (GEMV and MFMA), passed by value.
+struct RunArgs {
+  const void* A;        // [M, K]
+  const uint4* W;       // packed superblocks
+  const void* S;        // scales (half) or (scale, zero) half2 pairs, [G][Npad]
+  void* C;              // [M, N] fp16 or int32
+  void* ws;             // fp32/int32 workspace
+  int32_t M, N, K;
+  int32_t Npad, NB, nkb;
+  int32_t group_size;   // 0, -1 or g
+  int32_t smode;        // ScaleMode
+  int32_t zeros;        // 0/1
+  int32_t out_mode;     // OutMode
+  int32_t k_parts;
+  int32_t unit_kb;      // superblocks per split unit
+  int32_t n_units;      // nkb / unit_kb
+  int32_t waves;        // GEMV: waves per workgroup (K split inside the workgroup)
+};
+
+// kernel launchers (return hipSuccess or the launch error)
+hipError_t launch_pack(const Layout& L, const void* w, const void* s, const void* z, void* packed,
+                       hipStream_t st);
+hipError_t launch_gemv(int fmt, const RunArgs& a, hipStream_t st);
+hipError_t launch_mfma(int fmt, int tile, const RunArgs& a, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st);
+
+// MFMA tile configurations (BM x BN, waves WM x WN)
+enum Tile : int { TILE_32x64 = 0, TILE_64x64 = 1, TILE_128x128 = 2, TILE_COUNT = 3 };
+void tile_dims(int tile, int* bm, int* bn);
+
+}  // namespace qg

@@ -1,0 +1,68 @@
+// Split-K helpers: zeroing of the atomic accumulator (a fill kernel rather than
+// a memset so that callers may capture qgemm_run in a HIP graph), the fp32 -> fp16
+// conversion after atomic accumulation, and the fixed-order two-pass reduction
+// of per-part partials (the deterministic alternative to the atomic reduction
+// of hidet issue #364's parallel-k).
+#include "qgemm_internal.hpp"
+
+namespace qg {
+namespace {
+
+__global__ void fill_zero_kernel(uint4* __restrict__ p, size_t n16, uint32_t* __restrict__ tail,
+                                 size_t n4tail) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < n4tail) tail[threadIdx.x] = 0;
+}
+
+// C = fp16(sum over parts of ws[p]) (fp16 output) or int32 sum; parts = 1 for the
+// conversion after atomics.  Parts are added in order 0, 1, ..., so the result
+// does not depend on scheduling.
+template <bool FP>
+__global__ void finalize_kernel(const void* __restrict__ ws, void* __restrict__ C, size_t mn, int parts) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < mn; i += stride) {
+    if constexpr (FP) {
+      const float* w = static_cast<const float*>(ws);
+      float s = w[i];
+      for (int p = 1; p < parts; ++p) s += w[(size_t)p * mn + i];
+      static_cast<_Float16*>(C)[i] = (_Float16)s;
+    } else {
+      const int* w = static_cast<const int*>(ws);
+      int s = w[i];
+      for (int p = 1; p < parts; ++p) s += w[(size_t)p * mn + i];
+      static_cast<int*>(C)[i] = s;
+    }
+  }
+}
+
+int grid_for(size_t items, int threads) {
+  size_t b = (items + threads - 1) / threads;
+  if (b > 8192) b = 8192;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  // bytes is a multiple of 4 (fp32 / int32 elements)
+  const size_t n16 = bytes / 16, n4tail = (bytes % 16) / 4;
+  uint32_t* tail = reinterpret_cast<uint32_t*>(static_cast<char*>(p) + n16 * 16);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n16 ? n16 : 1, 256)), dim3(256), 0, st,
+                     static_cast<uint4*>(p), n16, tail, n4tail);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st) {
+  const size_t mn = (size_t)a.M * a.N;
+  const int parts = a.out_mode == OUT_PARTIAL ? a.k_parts : 1;
+  if (out_f16)
+    hipLaunchKernelGGL(finalize_kernel<true>, dim3(grid_for(mn, 256)), dim3(256), 0, st, a.ws, a.C, mn, parts);
+  else
+    hipLaunchKernelGGL(finalize_kernel<false>, dim3(grid_for(mn, 256)), dim3(256), 0, st, a.ws, a.C, mn, parts);
+  return hipGetLastError();
+}
+
+}  // namespace qg

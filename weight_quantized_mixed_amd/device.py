@@ -1,0 +1,87 @@
+"""torch device-tensor wrapper around the C ABI (marshalling only).
+
+PyTorch provides device memory and the stream; every computation is a
+libqgemm kernel.  Non-GPU tensors are rejected: there is no host fallback.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import qgemm as _q
+
+A_DTYPE = {"i4": "f16", "u4": "f16", "f16": "f16", "i8": "i8", "i2": "i8"}
+OUT_DTYPE = {"f16": ("f16", "f32"), "i8": ("i32", "i32")}
+
+
+def _ptr(t):
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("qgemm takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("qgemm takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def host_to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
+    """Copy a numpy array to the device; uint32 words travel as int32 bits."""
+    if arr is None:
+        return None
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(device)
+
+
+class QGemm:
+    """One plan: C[M,N] = A[M,K] . dequant(W) for a fixed shape and format."""
+
+    def __init__(self, M, N, K, w_dtype, group_size=0, has_zeros=False, k_parts=1,
+                 deterministic=False, device="cuda"):
+        self.M, self.N, self.K, self.w_dtype = int(M), int(N), int(K), w_dtype
+        self.a_dtype = A_DTYPE[w_dtype]
+        self.out_dtype, self.accum_dtype = OUT_DTYPE[self.a_dtype]
+        self.device = torch.device(device)
+        flags = _q.QGEMM_DETERMINISTIC if deterministic else 0
+        self.plan, self.packed_bytes, self.ws_bytes = _q.qgemm_create(
+            M, N, K, self.a_dtype, w_dtype, self.out_dtype, self.accum_dtype, group_size,
+            int(bool(has_zeros)), k_parts, flags)
+        self.path = _q.qgemm_plan_path(self.plan)
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "plan", None):
+            _q.qgemm_destroy(self.plan)
+            self.plan = None
+
+    __del__ = close
+
+    def pack(self, w, s=None, z=None, out=None, stream=None):
+        if out is None:
+            out = torch.empty(self.packed_bytes, dtype=torch.uint8, device=self.device)
+        _q.qgemm_pack_weights(self.plan, _ptr(w), _ptr(s), _ptr(z), _ptr(out), _stream(stream))
+        return out
+
+    def workspace(self):
+        if self.ws_bytes and self._ws is None:
+            self._ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def new_output(self):
+        dt = torch.float16 if self.out_dtype == "f16" else torch.int32
+        return torch.empty((self.M, self.N), dtype=dt, device=self.device)
+
+    def run(self, A, packed, C=None, ws=None, stream=None):
+        if C is None:
+            C = self.new_output()
+        if ws is None:
+            ws = self.workspace()
+        _q.qgemm_run(self.plan, _ptr(A), _ptr(packed), _ptr(C), _ptr(ws),
+                     0 if ws is None else ws.numel(), _stream(stream))
+        return C
