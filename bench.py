@@ -1,0 +1,245 @@
+"""Benchmark of the weight-quantized matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-grid] [--no-cpu]
+
+Workload (one "step" = one qgemm_run): W4A16 decode GEMV, M = 1, N = K = 16384,
+signed int4 weights with fp16 scales per group of 128 along K, fp16 out, fp32
+accumulation, k_parts = 1 — the M = 1 point of the pages' N = K = 16384 grid
+(BitBLAS issue #252 benchmark shapes).  Inputs are seeded synthetic data with
+the stated distributions, resident in HBM before timing starts.  A ring of
+packed-weight copies larger than twice the 256 MB Infinity Cache is cycled so
+that no call reads its weights from cache.
+
+Prints ONE JSON line: value = achieved algorithmic HBM bandwidth of the
+workload (GB/s); `roofline` for its kernel; `grid` with the µs, TFLOP/s or
+TOP/s, GB/s and roofline fraction of every other configuration of the grid
+(M = 1..16384 at N = K = 16384, and the LLaMA-7B projection shapes of hidet
+issue #364); `cpu_baseline` = the CPU oracle on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12                 # B/s
+PEAK = {"f16": 2.5e15, "i8": 5.0e15}   # dense MFMA FLOP/s (OP/s for int8)
+BITS = {"i4": 4, "u4": 4, "i2": 2, "i8": 8, "f16": 16}
+MALL_BYTES = 256 << 20
+METRIC = "qgemm µs + TFLOPS/TOPS + HBM GB/s vs roofline, M=1..16384, N=K=16384"
+
+
+def alg_bytes(M, N, K, w_dtype, g, zeros):
+    """Bytes the computation must move at least once: packed W, scales, zeros, A, C."""
+    G = 0 if g == 0 else (1 if g < 0 else K // g)
+    a_sz = 2 if w_dtype in ("i4", "u4", "f16") else 1
+    c_sz = 2 if a_sz == 2 else 4
+    return (N * K * BITS[w_dtype]) // 8 + N * G * 2 * (2 if zeros else 1) + M * K * a_sz + M * N * c_sz
+
+
+def label(c):
+    s = f"{c['w']} M={c['M']} N={c['N']} K={c['K']}"
+    if c.get("g"):
+        s += f" g={c['g']}"
+    if c.get("zeros"):
+        s += " zeros"
+    if c.get("kp", 1) > 1:
+        s += f" kp={c['kp']}"
+    return s
+
+
+_WEIGHTS = {}
+
+
+def _weights(c, q, seed):
+    """Packed weight ring for (format, N, K, g, zeros), shared by every M of the grid."""
+    import numpy as np
+    import synth
+    from weight_quantized_mixed_amd.device import host_to_device
+    key = (c["w"], c["N"], c["K"], c.get("g", 0), c.get("zeros", False))
+    if key not in _WEIGHTS:
+        p = synth.make_problem(1, c["N"], c["K"], c["w"], group_size=c.get("g", 0),
+                               has_zeros=c.get("zeros", False), seed=seed,
+                               A=np.zeros((1, c["K"]), dtype=np.float16 if c["w"] in ("i4", "u4", "f16") else np.int8))
+        packed = q.pack(host_to_device(p.w), host_to_device(p.s), host_to_device(p.z))
+        n_ring = 1 if q.packed_bytes >= 2 * MALL_BYTES else -(-(4 * MALL_BYTES) // q.packed_bytes)
+        _WEIGHTS[key] = [packed] + [packed.clone() for _ in range(min(n_ring, 64) - 1)]
+    return _WEIGHTS[key]
+
+
+class Bench:
+    """A configuration resident on the device with a ring of weight copies."""
+
+    def __init__(self, c, seed):
+        import torch
+        import synth
+        from weight_quantized_mixed_amd.device import QGemm, host_to_device
+        self.c = c
+        M, N, K, wd = c["M"], c["N"], c["K"], c["w"]
+        g, z, kp = c.get("g", 0), c.get("zeros", False), c.get("kp", 1)
+        if wd not in ("i4", "u4"):
+            g = 0
+        self.q = QGemm(M, N, K, wd, g, z, kp)
+        self.packed = _weights(c, self.q, seed)
+        A = host_to_device(synth.draw_activations(M, K, self.q.a_dtype, seed + M))
+        n_a = 1 if A.numel() * A.element_size() >= 2 * MALL_BYTES else len(self.packed)
+        self.As = [A] + [A.clone() for _ in range(n_a - 1)]
+        self.C = self.q.new_output()
+        self.ws = self.q.workspace()
+        self.i = 0
+        self.bytes = alg_bytes(M, N, K, wd, g, z)
+        self.flops = 2.0 * M * N * K
+        self.a_kind = "f16" if wd in ("i4", "u4", "f16") else "i8"
+        torch.cuda.synchronize()
+
+    def call(self):
+        j = self.i
+        self.i += 1
+        self.q.run(self.As[j % len(self.As)], self.packed[j % len(self.packed)], self.C, self.ws)
+
+    def timed(self, n):
+        """Seconds per call over n back-to-back calls (HIP events on the launch stream)."""
+        import torch
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(n):
+            self.call()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    def roof(self, t):
+        t_hbm = self.bytes / HBM_PEAK
+        t_mfma = self.flops / PEAK[self.a_kind]
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        return bound, max(t_hbm, t_mfma) / t
+
+    def close(self):
+        self.q.close()
+
+
+def measure_grid_entry(b, bursts=15):
+    import statistics
+    b.timed(5)
+    per = max(len(b.packed), 8)
+    if b.flops > 1e12:
+        per, bursts = 2, 5
+    samples = sorted(b.timed(per) for _ in range(bursts))
+    t = statistics.median(samples)
+    bound, frac = b.roof(t)
+    return {"config": label(b.c), "us": round(t * 1e6, 3),
+            "p10_us": round(samples[max(0, len(samples) // 10)] * 1e6, 3),
+            "p90_us": round(samples[min(len(samples) - 1, (9 * len(samples)) // 10)] * 1e6, 3),
+            ("TFLOPS" if b.a_kind == "f16" else "TOPS"): round(b.flops / t / 1e12, 3),
+            "GBps": round(b.bytes / t / 1e9, 1), "bound": bound, "roofline_frac": round(frac, 4),
+            "path": "gemv" if b.q.path == 1 else "mfma"}
+
+
+GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128, 512)]
+        + [{"w": "i4", "M": 1, "N": 16384, "K": 16384, "g": 128, "kp": 4}]
+        + [{"w": w, "M": M, "N": 16384, "K": 16384, "kp": kp} for w in ("i8", "i2")
+           for M in (1, 32, 128, 512) for kp in (1, 4)]
+        + [{"w": "f16", "M": M, "N": 16384, "K": 16384} for M in (1, 32, 128, 512)]
+        + [{"w": "i4", "M": M, "N": N, "K": K, "g": 128, "kp": kp} for M in (1, 128)
+           for (K, N) in ((4096, 11008), (11008, 4096), (4096, 4096), (4096, 32000)) for kp in (1, 4)]
+        + [{"w": "i4", "M": 1, "N": 4096, "K": 4096, "g": 128}]
+        + [{"w": "f16", "M": 16384, "N": 16384, "K": 16384},
+           {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}])
+
+
+def cpu_baseline(c, seed):
+    """The CPU oracle, as it stands, on the benchmark workload (one full step)."""
+    import numpy as np
+    import oracle
+    import synth
+    p = synth.make_problem(c["M"], c["N"], c["K"], c["w"], group_size=c.get("g", 0), seed=seed)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = None
+    t0 = time.perf_counter()
+    oracle.qgemm_ref(p.A, p.w, p.s, p.z, N=p.N, K=p.K, w_dtype=p.w_dtype, group_size=p.group_size)
+    dt = time.perf_counter() - t0
+    nbytes = alg_bytes(c["M"], c["N"], c["K"], c["w"], c.get("g", 0), False)
+    # the unpack and dequantisation (nearly all of the time) are single-threaded numpy
+    # element-wise passes; only the final float64 product goes through BLAS threads
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": f"one full step ({label(c)}), {dt:.2f} s, float64 numpy",
+            "seconds": round(dt, 3), "blas_threads": blas, "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-grid", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="", help="substring filter on grid entries")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path does not "
+              "shard across GPUs here)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    import synth
+    torch.cuda.set_device(0)
+
+    head = {"w": "i4", "M": 1, "N": 16384, "K": 16384, "g": 128}
+    print(f"[bench] workload {label(head)}", file=sys.stderr, flush=True)
+    hb = Bench(head, synth.seed_for(5))
+    for _ in range(args.warmup):
+        hb.call()
+    torch.cuda.synchronize()
+    t_call = hb.timed(args.steps)          # barrier + synchronize on both sides (one rank)
+    torch.cuda.synchronize()
+    bound, frac = hb.roof(t_call)
+    achieved = hb.bytes / t_call
+    out = {
+        "metric": METRIC, "value": round(achieved / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_call * 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded; A~N(0,1) fp16, q~U[-8,7], s~U[0.005,0.02] fp16)",
+        "config": {"workload": "W4A16 GEMV M=1 N=16384 K=16384 g=128 k_parts=1", "M": 1, "N": 16384,
+                   "K": 16384, "group_size": 128, "k_parts": 1, "ring_copies": len(hb.packed),
+                   "us_per_call": round(t_call * 1e6, 3)},
+        "roofline": {"bound": bound, "achieved": round(achieved / 1e9, 2), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(frac, 4), "traffic": None,
+                     "alg_bytes_per_launch": hb.bytes, "kernel": "gemv_kernel<FMT_I4, 1>"},
+    }
+    hb.close()
+    del hb
+    _WEIGHTS.clear()
+    torch.cuda.empty_cache()
+    print(f"[bench] headline {out['config']['us_per_call']} us, {out['value']} GB/s", file=sys.stderr, flush=True)
+
+    if not args.no_grid:
+        grid = []
+        for i, c in enumerate(GRID):
+            if args.only and args.only not in label(c):
+                continue
+            b = Bench(c, synth.seed_for(6, i))
+            grid.append(measure_grid_entry(b))
+            print(f"[bench] {grid[-1]}", file=sys.stderr, flush=True)
+            b.close()
+            del b
+            time.sleep(0.05)   # gap between configurations
+        out["grid"] = grid
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(head, synth.seed_for(5))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
