@@ -57,22 +57,32 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
   return QGEMM_OK;
 }
 
+#ifndef QG_GEMV_TARGET_WAVES
+#define QG_GEMV_TARGET_WAVES 2048
+#endif
+
 int choose_gemv_waves(const qgemm_plan* p) {
   const int64_t rb = (p->N + 63) / 64;
   const int64_t per_part = p->L.nkb / p->k_parts;
-  int64_t want = (2048 + rb * p->k_parts - 1) / (rb * p->k_parts);
+  int64_t want = (QG_GEMV_TARGET_WAVES + rb * p->k_parts - 1) / (rb * p->k_parts);
   int64_t maxw = per_part / 2;
   if (maxw < 1) maxw = 1;
-  if (maxw > 16) maxw = 16;
+  if (maxw > GEMV_MAX_WAVES) maxw = GEMV_MAX_WAVES;
   if (want > maxw) want = maxw;
   if (want < 1) want = 1;
   return (int)want;
 }
 
+// Largest tile that still gives every CU a workgroup (256 CUs).
 int choose_tile(const qgemm_plan* p) {
   if (p->M <= 32) return TILE_32x64;
-  const int64_t big = ((p->M + 127) / 128) * ((p->N + 127) / 128) * p->k_parts;
-  return big >= 256 ? TILE_128x128 : TILE_64x64;
+  auto wgs = [&](int tile) {
+    int bm, bn;
+    tile_dims(p->L.fmt, tile, &bm, &bn);
+    return ((p->M + bm - 1) / bm) * ((p->N + bn - 1) / bn) * p->k_parts;
+  };
+  if (p->M >= 256 && wgs(TILE_BIG) >= 256) return TILE_BIG;
+  return wgs(TILE_128x128) >= 256 ? TILE_128x128 : TILE_64x64;
 }
 
 RunArgs make_args(const qgemm_plan* p, const void* A, const void* packed, void* C, void* ws) {
@@ -96,6 +106,7 @@ RunArgs make_args(const qgemm_plan* p, const void* A, const void* packed, void* 
   a.unit_kb = p->unit_kb;
   a.n_units = p->n_units;
   a.waves = p->gemv_waves;
+  a.sb_per_group = p->group_size > KB ? p->group_size / KB : p->group_size < 0 ? (int32_t)p->L.nkb : 1;
   a.out_mode = p->k_parts == 1 ? OUT_STORE : (p->flags & QGEMM_DETERMINISTIC) ? OUT_PARTIAL : OUT_ATOMIC;
   return a;
 }
@@ -134,6 +145,9 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   if (has_zeros && (fmt != FMT_U4 || group_size == 0)) return QGEMM_ERR_UNSUPPORTED;
   if (group_size > 0 && (K % group_size != 0 || group_size % 32 != 0)) return QGEMM_ERR_UNSUPPORTED;
   if (K % KB != 0) return QGEMM_ERR_UNSUPPORTED;
+
+  // kernels index the blob with 32-bit uint4 offsets
+  if ((N + 255) / 256 * 256 / 16 * (K / KB) * 64 >= INT32_MAX) return QGEMM_ERR_UNSUPPORTED;
 
   const int64_t unit = group_size > KB ? group_size : KB;
   const int64_t n_units = K / unit;
@@ -174,6 +188,7 @@ qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const voi
   if (plan->L.G && !scales) return QGEMM_ERR_INVALID_ARG;
   if (plan->L.zeros && !zeros) return QGEMM_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(packed)) & 15) return QGEMM_ERR_INVALID_ARG;
+  (void)hipGetLastError();  // clear an error left by an unrelated earlier call on this thread
   hipError_t e = launch_pack(plan->L, w, scales, zeros, packed, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_DEVICE;
 }
@@ -187,6 +202,7 @@ qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed
     return QGEMM_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   RunArgs a = make_args(plan, A, packed, C, workspace);
+  (void)hipGetLastError();  // clear an error left by an unrelated earlier call on this thread
   const bool out_f16 = plan->out_dtype == QGEMM_F16;
   hipError_t e = hipSuccess;
   if (a.out_mode == OUT_ATOMIC)

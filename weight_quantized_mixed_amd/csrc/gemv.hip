@@ -2,16 +2,29 @@
 //
 // Each workgroup owns 64 output columns (four 16-column superblock columns)
 // and one k-part; its waves split the part's superblocks into contiguous runs
-// and meet in LDS at the end (the intra-workgroup "block reduction" whose
-// absence the BitBLAS issue #252 split-K discussion blames for the slow
-// M = 32/128 dequantised rows).  Lane l owns column n = 64*rb + l: for every
-// superblock it loads the four 16-byte pieces of its column (one wave-wide load
-// per quarter reads 4 x 256 contiguous bytes), unpacks them in registers (the
-// packed-upcast trick of hidet issue #364) and dots them with the activation
-// slice.  All lanes of a wave need the same activations, so A is read through
-// the scalar unit (constant address space) and never occupies vector memory
-// bandwidth.  k-parts > 1 reduce across workgroups with global atomics or a
-// two-pass partial store (hidet issue #364, parallel-k with atomic reduction).
+// and meet in LDS at the end (the intra-workgroup "block reduction" that the
+// BitBLAS issue #252 discussion names as the cure for slow skinny dequantised
+// shapes).  Lane l owns column n = 64*rb + l: for every superblock it loads
+// the four 16-byte pieces of its column (one wave-wide load per quarter reads
+// 4 x 256 contiguous bytes), unpacks them in registers (the packed-upcast
+// trick of hidet issue #364) and dots them with the activation slice.  The
+// loads of the next superblocks are issued before the current ones are
+// consumed (two register stages), so every wave keeps 128 bytes per lane in
+// flight while it computes.  All lanes of a wave need the same activations,
+// so A is read through the scalar unit (constant address space).
+//
+// Bias folding.  The packed int4 nibble v (offset-binary) becomes the fp16
+// 1024 + v with one and-or, and 1024 + 16v when taken from the upper nibble of
+// a byte, so no per-element subtraction is needed: per superblock and row,
+//   sum a*q = accE + accO/16 - (1024 + b)*SE - (64 + b)*SO,
+// where accE / accO are the dot products of the two nibble classes, SE / SO the
+// sums of the activations over the positions of each class, and b the
+// offset (8 for signed, 0 for unsigned).  int2 crumbs are masked in place
+// (byte values c, 4c, 16c, and the two's complement top crumb as 64q), dotted
+// with int8 activations into four accumulators, and recombined exactly.  The
+// activation sums come from one load per lane and a DPP reduction per
+// superblock.  k-parts > 1 reduce across workgroups with global atomics or a
+// two-pass partial store (hidet issue #364, parallel-k).
 #include "qgemm_internal.hpp"
 
 namespace qg {
@@ -23,15 +36,64 @@ typedef const __attribute__((address_space(4))) uint32_t* cptr;
 __device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
 __device__ __forceinline__ float h2f(uint16_t x) { return (float)__builtin_bit_cast(_Float16, x); }
 
-template <int FMT, int MR>
-__global__ __launch_bounds__(1024) void gemv_kernel(RunArgs a) {
-  constexpr bool FP = (FMT == FMT_I4 || FMT == FMT_U4 || FMT == FMT_F16);
-  typedef typename std::conditional<FP, float, int>::type acc_t;
-  constexpr int KB = kb_of(FMT);
-  // dwords of A per row: fp16 -> K/2, int8 -> K/4
-  const int a_row_dw = FP ? a.K / 2 : a.K / 4;
+// (x & m) | c in one VALU op (the masks are not inline constants, so they are
+// passed in registers)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Weights are read exactly once: non-temporal loads keep them from displacing
+// the activations and scales in the caches.
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp_add(T v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true);
+  return v + __builtin_bit_cast(T, moved);
+}
+
+// After this, lane 31 holds the sum over lanes 0..31 and lane 63 the sum over
+// lanes 32..63 (in-row inclusive scans by row_shr 1, 2, 4, 8, then row_bcast15
+// into rows 1 and 3).
+template <typename T>
+__device__ __forceinline__ T half_wave_sums(T v) {
+  v = dpp_add<0x111, 0xF>(v);
+  v = dpp_add<0x112, 0xF>(v);
+  v = dpp_add<0x114, 0xF>(v);
+  v = dpp_add<0x118, 0xF>(v);
+  v = dpp_add<0x142, 0xA>(v);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T lane_value(T v, int lane) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// VAR (int4 only): 0 folded, unscaled; 1 folded with one scale group per
+// superblock; 2 as 1 with zero points; 3 exact per-element conversion with a
+// scale group per 32-position piece (group size 32 or 64).  int2 is always folded.
+template <int FMT, int MR, int VAR>
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
+  constexpr bool FOLD = (FMT == FMT_I2) || ((FMT == FMT_I4 || FMT == FMT_U4) && VAR != 3);
+  constexpr bool SCALED = VAR == 1 || VAR == 2;
+  constexpr bool ZEROS = VAR == 2;
+  constexpr bool FP = (FMT == FMT_I4 || FMT == FMT_U4 || FMT == FMT_F16);
+  constexpr bool I4 = (FMT == FMT_I4 || FMT == FMT_U4);
+  typedef typename std::conditional<FP, float, int>::type acc_t;
+  // dwords of A per row: fp16 -> K/2, int8 -> K/4; every superblock is 64 dwords of A per row
+  const int a_row_dw = FP ? a.K / 2 : a.K / 4;
+  constexpr int A_DW_SB = (FMT == FMT_F16) ? 16 : (FMT == FMT_I8) ? 16 : 64;
+
+  const int lane = threadIdx.x & 63;
+  // uniform within a wave: keeps the K range and activation addresses scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rb = blockIdx.x, part = blockIdx.y;
   const int n = rb * 64 + lane;
 
@@ -43,59 +105,131 @@ __global__ __launch_bounds__(1024) void gemv_kernel(RunArgs a) {
   const int my1 = min(my0 + per, kb1);
 
   cptr A = (cptr)a.A;
+  const uint32_t* __restrict__ Av = static_cast<const uint32_t*>(a.A);
   const uint4* __restrict__ Wl = a.W + (size_t)(rb * 4 + (lane >> 4)) * 64 + (lane & 15);
-  const size_t sb_stride = (size_t)a.NB * 64;  // uint4 per superblock row (kb)
+  // 32-bit offsets: the blob is far below 2^31 uint4 and A below 2^31 dwords
+  const uint32_t sb_stride = (uint32_t)a.NB * 64u;  // uint4 per superblock row (kb)
+  const uint32_t a_row = (uint32_t)a_row_dw;
+  // activation dword this lane feeds into the per-superblock class sums
+  const int sum_dw = (FMT == FMT_I2) ? lane : (lane < 32 ? 2 * lane : 2 * (lane - 32) + 1);
 
   acc_t tot[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) tot[m] = 0;
 
-  auto do_block = [&](const uint4 (&wv)[4], int kb) {
-    if constexpr (FMT == FMT_I4 || FMT == FMT_U4) {
+  constexpr int UNR = QG_GEMV_UNR;
+  struct Stage {
+    uint4 w[UNR][4];
+    uint32_t as[UNR][MR];
+    uint32_t sc[UNR];  // raw scale (or scale | zero << 16) of the superblock's group
+  };
+
+  // Every stage issues the same loads (superblocks past the wave's range re-read
+  // its last one and are not used), so the compiler can count outstanding loads
+  // exactly and never has to drain the next stage to use this one.
+  auto load = [&](Stage& s, int kb) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const uint32_t kbl = (uint32_t)min(kb + u, my1 - 1);
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) s.w[u][kq] = stream_load(&Wl[kbl * sb_stride + kq * 16]);
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) s.as[u][m] = Av[m * a_row + kbl * A_DW_SB + sum_dw];
+      }
+      if constexpr (SCALED) {
+        // group of the superblock: sb_per_group = g / 128 (nkb when one group spans K)
+        const uint32_t grp = a.sb_per_group == 1 ? kbl : kbl / (uint32_t)a.sb_per_group;
+        if constexpr (ZEROS) s.sc[u] = static_cast<const uint32_t*>(a.S)[grp * (uint32_t)a.Npad + n];
+        else s.sc[u] = static_cast<const uint16_t*>(a.S)[grp * (uint32_t)a.Npad + n];
+      } else {
+        s.sc[u] = 0x3C00u;  // 1.0
+      }
+    }
+  };
+
+  auto scale_of = [&](int grp, float& s, float& z) {
+    if (a.zeros) {
+      const uint32_t sz = static_cast<const uint32_t*>(a.S)[(size_t)grp * a.Npad + n];
+      s = h2f((uint16_t)(sz & 0xFFFF));
+      z = h2f((uint16_t)(sz >> 16));
+    } else {
+      s = h2f(static_cast<const uint16_t*>(a.S)[(size_t)grp * a.Npad + n]);
+      z = 0.f;
+    }
+  };
+
+  auto do_block = [&](const uint4 (&wv)[4], const uint32_t (&as)[MR], uint32_t sc, int kb) {
+    if constexpr (I4 && FOLD) {
+      const uint32_t MASK_E = 0x000F000Fu, MASK_O = 0x00F000F0u, EXP16 = 0x64006400u;
+      float accE[MR], accO[MR];
+#pragma unroll
+      for (int m = 0; m < MR; ++m) { accE[m] = 0.f; accO[m] = 0.f; }
+      // the superblock's activations first (64 scalar dwords per row), so their
+      // latency overlaps the nibble unpacking below
+      uint32_t av[MR][64];
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int i = 0; i < 64; ++i) av[m][i] = A[m * a_row + kb * 64 + i];
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const uint32_t wd[4] = {wv[kq].x, wv[kq].y, wv[kq].z, wv[kq].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = wd[t], w8 = w >> 8;
+          const half2v e0 = as_h2(and_or(w, MASK_E, EXP16)), o0 = as_h2(and_or(w, MASK_O, EXP16));
+          const half2v e1 = as_h2(and_or(w8, MASK_E, EXP16)), o1 = as_h2(and_or(w8, MASK_O, EXP16));
+          const int base = kq * 16 + 4 * t;  // activation dword of positions 8t, 8t+1
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            accE[m] = __builtin_amdgcn_fdot2(e0, as_h2(av[m][base + 0]), accE[m], false);
+            accO[m] = __builtin_amdgcn_fdot2(o0, as_h2(av[m][base + 1]), accO[m], false);
+            accE[m] = __builtin_amdgcn_fdot2(e1, as_h2(av[m][base + 2]), accE[m], false);
+            accO[m] = __builtin_amdgcn_fdot2(o1, as_h2(av[m][base + 3]), accO[m], false);
+          }
+        }
+      }
+      constexpr float cE = (FMT == FMT_I4) ? 1032.f : 1024.f, cO = (FMT == FMT_I4) ? 72.f : 64.f;
+      const float s = h2f((uint16_t)(sc & 0xFFFFu)), z = h2f((uint16_t)(sc >> 16));
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const float h = half_wave_sums(__builtin_amdgcn_fdot2(as_h2(as[m]), as_h2(0x3C003C00u), 0.f, false));
+        const float SE = lane_value(h, 31), SO = lane_value(h, 63);
+        float v = accE[m] + accO[m] * 0.0625f - cE * SE - cO * SO;
+        if constexpr (ZEROS) v -= z * (SE + SO);
+        tot[m] += SCALED ? s * v : v;
+      }
+    } else if constexpr (I4) {
+      // exact per-element conversion, used when a superblock holds several groups
       constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;  // 1032 or 1024
       const half2v hb = as_h2(bias);
-      float pq[MR], pa[MR];
-#pragma unroll
-      for (int m = 0; m < MR; ++m) { pq[m] = 0.f; pa[m] = 0.f; }
-      auto flush = [&](int grp) {
-        if (a.smode == SC_NONE) {
-#pragma unroll
-          for (int m = 0; m < MR; ++m) tot[m] += pq[m];
-        } else if (a.zeros) {
-          const uint32_t sz = static_cast<const uint32_t*>(a.S)[(size_t)grp * a.Npad + n];
-          const float s = h2f((uint16_t)(sz & 0xFFFF)), z = h2f((uint16_t)(sz >> 16));
-#pragma unroll
-          for (int m = 0; m < MR; ++m) tot[m] += s * (pq[m] - z * pa[m]);
-        } else {
-          const float s = h2f(static_cast<const uint16_t*>(a.S)[(size_t)grp * a.Npad + n]);
-#pragma unroll
-          for (int m = 0; m < MR; ++m) tot[m] += s * pq[m];
-        }
-#pragma unroll
-        for (int m = 0; m < MR; ++m) { pq[m] = 0.f; pa[m] = 0.f; }
-      };
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
         const uint32_t wd[4] = {wv[kq].x, wv[kq].y, wv[kq].z, wv[kq].w};
         const int k0 = kb * 128 + kq * 32;
+        float pq[MR], pa[MR];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int m = 0; m < MR; ++m) { pq[m] = 0.f; pa[m] = 0.f; }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t h = ((wd[t] >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
             const half2v q = as_h2(h) - hb;  // exact small integers
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
-              const uint32_t av = A[(size_t)m * a_row_dw + (k0 >> 1) + 4 * t + j];
+              const uint32_t av = A[m * a_row + (k0 >> 1) + 4 * t + j];
               pq[m] = __builtin_amdgcn_fdot2(q, as_h2(av), pq[m], false);
               if (FMT == FMT_U4 && a.zeros)
                 pa[m] = __builtin_amdgcn_fdot2(as_h2(0x3C003C00u), as_h2(av), pa[m], false);
             }
           }
-        }
-        if (a.smode == SC_PIECE) flush(k0 / a.group_size);
+        float s, z;
+        scale_of(k0 / a.group_size, s, z);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) tot[m] += s * (pq[m] - z * pa[m]);
       }
-      if (a.smode != SC_PIECE) flush(a.group_size > 0 ? (kb * 128) / a.group_size : 0);
     } else if constexpr (FMT == FMT_F16) {
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
@@ -105,7 +239,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(RunArgs a) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
-            const uint32_t av = A[(size_t)m * a_row_dw + (k0 >> 1) + t];
+            const uint32_t av = A[m * a_row + (k0 >> 1) + t];
             tot[m] = __builtin_amdgcn_fdot2(as_h2(wd[t]), as_h2(av), tot[m], false);
           }
       }
@@ -118,52 +252,68 @@ __global__ __launch_bounds__(1024) void gemv_kernel(RunArgs a) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
-            const uint32_t av = A[(size_t)m * a_row_dw + (k0 >> 2) + t];
+            const uint32_t av = A[m * a_row + (k0 >> 2) + t];
             tot[m] = __builtin_amdgcn_sdot4((int)wd[t], (int)av, tot[m], false);
           }
       }
     } else {  // FMT_I2
+      int acc[4][MR];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[j][m] = 0;
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
         const uint32_t wd[4] = {wv[kq].x, wv[kq].y, wv[kq].z, wv[kq].w};
-        const int k0 = kb * 256 + kq * 64;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t) {
+          // byte b of (w & mask_j) is position 4j + b scaled by 4^j; the top crumb is
+          // stored two's complement, so its byte is exactly 64q as a signed int8
+          const int q0 = (int)(wd[t] & 0x03030303u), q1 = (int)(wd[t] & 0x0C0C0C0Cu);
+          const int q2 = (int)(wd[t] & 0x30303030u), q3 = (int)(wd[t] & 0xC0C0C0C0u);
+          const int base = kq * 16 + 4 * t;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            // offset-binary crumbs 0..3 -> signed bytes -2..1 through a byte-permute table
-            const uint32_t sel = (wd[t] >> (2 * j)) & 0x03030303u;
-            const int qv = (int)__builtin_amdgcn_perm(0u, 0x0100FFFEu, sel);
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-              const uint32_t av = A[(size_t)m * a_row_dw + (k0 >> 2) + 4 * t + j];
-              tot[m] = __builtin_amdgcn_sdot4(qv, (int)av, tot[m], false);
-            }
+          for (int m = 0; m < MR; ++m) {
+            cptr Am = A + (m * a_row + kb * 64 + base);
+            const uint4 a4 = make_uint4(Am[0], Am[1], Am[2], Am[3]);
+            acc[0][m] = __builtin_amdgcn_sdot4(q0, (int)a4.x, acc[0][m], false);
+            acc[1][m] = __builtin_amdgcn_sdot4(q1, (int)a4.y, acc[1][m], false);
+            acc[2][m] = __builtin_amdgcn_sdot4(q2, (int)a4.z, acc[2][m], false);
+            acc[3][m] = __builtin_amdgcn_sdot4(q3, (int)a4.w, acc[3][m], false);
           }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        // classes 0..2 are offset-binary (q + 2): subtract 2 * (their activation sum)
+        const int mine = (lane & 3) == 3 ? 0 : __builtin_amdgcn_sdot4((int)as[m], 0x01010101, 0, false);
+        const int h = half_wave_sums(mine);
+        const int S012 = lane_value(h, 31) + lane_value(h, 63);
+        tot[m] += acc[0][m] + (acc[1][m] >> 2) + (acc[2][m] >> 4) + (acc[3][m] >> 6) - 2 * S012;
       }
     }
   };
 
-  constexpr int UNR = 2;
+  // two register stages: loads of the next UNR superblocks fly while these are consumed
+  Stage s0, s1;
   int kb = my0;
-  for (; kb + UNR <= my1; kb += UNR) {
-    uint4 wv[UNR][4];
+  if (kb < my1) load(s0, kb);
+  while (kb < my1) {
+    load(s1, kb + UNR);
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
+      if (kb + u < my1) do_block(s0.w[u], s0.as[u], s0.sc[u], kb + u);
+    kb += UNR;
+    if (kb >= my1) break;
+    load(s0, kb + UNR);
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) wv[u][kq] = Wl[(size_t)(kb + u) * sb_stride + kq * 16];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) do_block(wv[u], kb + u);
-  }
-  for (; kb < my1; ++kb) {
-    uint4 wv[4];
-#pragma unroll
-    for (int kq = 0; kq < 4; ++kq) wv[kq] = Wl[(size_t)kb * sb_stride + kq * 16];
-    do_block(wv, kb);
+    for (int u = 0; u < UNR; ++u)
+      if (kb + u < my1) do_block(s1.w[u], s1.as[u], s1.sc[u], kb + u);
+    kb += UNR;
   }
 
   // block reduction across the waves of the workgroup
-  __shared__ acc_t red[16][MR][64];
+  __shared__ acc_t red[GEMV_MAX_WAVES][MR][64];
 #pragma unroll
   for (int m = 0; m < MR; ++m) red[wave][m][lane] = tot[m];
   __syncthreads();
@@ -186,12 +336,12 @@ __global__ __launch_bounds__(1024) void gemv_kernel(RunArgs a) {
   }
 }
 
-template <int FMT>
+template <int FMT, int VAR>
 hipError_t launch_fmt(const RunArgs& a, hipStream_t st) {
   dim3 grid((a.N + 63) / 64, a.k_parts), block(64 * a.waves);
   switch (a.M) {
 #define QG_CASE(R) \
-  case R: hipLaunchKernelGGL((gemv_kernel<FMT, R>), grid, block, 0, st, a); break;
+  case R: hipLaunchKernelGGL((gemv_kernel<FMT, R, VAR>), grid, block, 0, st, a); break;
     QG_CASE(1) QG_CASE(2) QG_CASE(3) QG_CASE(4) QG_CASE(5) QG_CASE(6) QG_CASE(7) QG_CASE(8)
 #undef QG_CASE
     default: return hipErrorInvalidValue;
@@ -202,12 +352,17 @@ hipError_t launch_fmt(const RunArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_gemv(int fmt, const RunArgs& a, hipStream_t st) {
+  const int var = a.smode == SC_PIECE ? 3 : a.smode == SC_NONE ? 0 : a.zeros ? 2 : 1;
   switch (fmt) {
-    case FMT_I4: return launch_fmt<FMT_I4>(a, st);
-    case FMT_U4: return launch_fmt<FMT_U4>(a, st);
-    case FMT_F16: return launch_fmt<FMT_F16>(a, st);
-    case FMT_I8: return launch_fmt<FMT_I8>(a, st);
-    case FMT_I2: return launch_fmt<FMT_I2>(a, st);
+    case FMT_I4:
+      return var == 3 ? launch_fmt<FMT_I4, 3>(a, st) : var == 0 ? launch_fmt<FMT_I4, 0>(a, st)
+                                                               : launch_fmt<FMT_I4, 1>(a, st);
+    case FMT_U4:
+      return var == 3 ? launch_fmt<FMT_U4, 3>(a, st) : var == 0 ? launch_fmt<FMT_U4, 0>(a, st)
+           : var == 1 ? launch_fmt<FMT_U4, 1>(a, st) : launch_fmt<FMT_U4, 2>(a, st);
+    case FMT_F16: return launch_fmt<FMT_F16, 0>(a, st);
+    case FMT_I8: return launch_fmt<FMT_I8, 0>(a, st);
+    case FMT_I2: return launch_fmt<FMT_I2, 0>(a, st);
   }
   return hipErrorInvalidValue;
 }

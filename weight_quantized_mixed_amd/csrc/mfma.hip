@@ -2,17 +2,24 @@
 //
 // fp16 activations use v_mfma_f32_16x16x32_f16 (fp32 accumulation); int8
 // activations use v_mfma_i32_16x16x64_i8 (exact int32 accumulation, the int8
-// product semantics of Triton PR #3595).  Every stage moves a BM x 256-byte
-// activation slab and BN/16 x KSTEP weight superblocks from HBM into one of
-// two LDS buffers while the other is consumed (multi-stage software pipelining
-// of hidet issue #364).  Packed weights are upcast in registers right before
-// the MFMA: int4 nibbles become fp16 by or-ing the 0x6400 exponent and
-// subtracting the bias exactly, then the group scale (and zero point) is
-// applied in fp16; int2 crumbs become int8 through a byte-permute table.
-// Since the pack kernel stores each 16-byte weight piece in the lane order of
-// the B operand (lane l: column l%16, K slice l/16), a B fragment is one
-// conflict-free 16-byte LDS read per lane; the A fragment of lane l reads row
-// l%16 at the matching K slice, so A and B agree on the K order by construction.
+// product semantics of Triton PR #3595).  Every stage moves a BM-row activation
+// slab and BN/16 x KSTEP weight superblocks from HBM into one of two LDS
+// buffers while the other is consumed (the multi-stage software pipelining of
+// hidet issue #364; the depth is two, the tile and stage depth depend on the
+// problem size).  Packed weights are upcast in registers right before the
+// MFMA: int4 nibbles become fp16 by or-ing the 0x6400 exponent and subtracting
+// the bias exactly, then the group scale (and zero point) is applied in fp16;
+// int2 crumbs become int8 through a byte-permute table.  Since the pack kernel
+// stores each 16-byte weight piece in the lane order of the B operand (lane l:
+// column l%16, K slice l/16), a B fragment is one conflict-free 16-byte LDS read
+// per lane; the A fragment of lane l reads row l%16 at the matching K slice, so
+// A and B agree on the K order by construction.
+//
+// Workgroups are numbered so that each of the 8 XCDs (which receive workgroups
+// round-robin) owns a contiguous band of output tiles, swept in column-major
+// groups of 8 tile rows: the A row-blocks and B column-blocks that concurrently
+// running workgroups share then stay in that XCD's L2 (the traversal / L2
+// reuse point made in the mKernel AG-GEMM PR #41 discussion).
 #include "qgemm_internal.hpp"
 
 namespace qg {
@@ -27,29 +34,37 @@ __device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(
 __device__ __forceinline__ uint32_t as_u32(half2v x) { return __builtin_bit_cast(uint32_t, x); }
 
 template <int FMT> struct FmtTraits;
-template <> struct FmtTraits<FMT_I4> { static constexpr int KSTEP = 1, E = 8, STEPS = 4; static constexpr bool FP = true; };
-template <> struct FmtTraits<FMT_U4> { static constexpr int KSTEP = 1, E = 8, STEPS = 4; static constexpr bool FP = true; };
-template <> struct FmtTraits<FMT_F16> { static constexpr int KSTEP = 4, E = 8, STEPS = 1; static constexpr bool FP = true; };
-template <> struct FmtTraits<FMT_I8> { static constexpr int KSTEP = 4, E = 16, STEPS = 1; static constexpr bool FP = false; };
-template <> struct FmtTraits<FMT_I2> { static constexpr int KSTEP = 1, E = 16, STEPS = 4; static constexpr bool FP = false; };
+// E: elements per lane per MFMA; STEPS: MFMA K-steps per superblock
+template <> struct FmtTraits<FMT_I4> { static constexpr int E = 8, STEPS = 4; static constexpr bool FP = true; };
+template <> struct FmtTraits<FMT_U4> { static constexpr int E = 8, STEPS = 4; static constexpr bool FP = true; };
+template <> struct FmtTraits<FMT_F16> { static constexpr int E = 8, STEPS = 1; static constexpr bool FP = true; };
+template <> struct FmtTraits<FMT_I8> { static constexpr int E = 16, STEPS = 1; static constexpr bool FP = false; };
+template <> struct FmtTraits<FMT_I2> { static constexpr int E = 16, STEPS = 4; static constexpr bool FP = false; };
+
+// superblocks per stage: 256 activation bytes per row, 128 for the 256-row tiles
+// of the fp16 and int8 weight formats (keeps two stages within LDS)
+constexpr int kstep_of(int fmt, int bm) {
+  return (fmt == FMT_I4 || fmt == FMT_U4 || fmt == FMT_I2) ? 1 : (bm >= 256 ? 2 : 4);
+}
 
 template <int FMT, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
   using T = FmtTraits<FMT>;
   constexpr bool FP = T::FP;
   constexpr int KB = kb_of(FMT);
-  constexpr int KSTEP = T::KSTEP, E = T::E, STEPS = T::STEPS;
+  constexpr int KSTEP = kstep_of(FMT, BM), E = T::E, STEPS = T::STEPS;
   constexpr int ESZ = FP ? 2 : 1;             // activation element bytes
-  constexpr int ROWB = KSTEP * KB * ESZ;      // activation bytes per row per stage (256)
-  constexpr int PITCH = ROWB + 16;            // padded LDS row pitch
+  constexpr int ROWB = KSTEP * KB * ESZ;      // activation bytes per row per stage
+  constexpr int PITCH = ROWB + 16;            // padded LDS row pitch (conflict-free fragment reads)
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM / 16, WTN = BN / WN / 16;
   constexpr int NBT = BN / 16;                // superblock columns per tile
-  constexpr int A_CHUNKS = BM * (ROWB / 16);  // 16-byte chunks per stage
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per activation row
+  constexpr int A_CHUNKS = BM * CPR;          // 16-byte chunks per stage
   constexpr int B_CHUNKS = KSTEP * NBT * 64;
   constexpr int A_PER = (A_CHUNKS + NT - 1) / NT;
   constexpr int B_PER = (B_CHUNKS + NT - 1) / NT;
-  static_assert(ROWB == 256, "one activation slab is 256 bytes per row");
+  static_assert(ROWB == 128 || ROWB == 256, "activation slab of 128 or 256 bytes per row");
   typedef typename std::conditional<FP, float4v, int4v>::type acc_v;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * PITCH];
@@ -57,8 +72,21 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, part = blockIdx.z;
   const int kq = lane >> 4, l16 = lane & 15;
+
+  // ---- tile of this workgroup (1-D grid: tiles x k-parts)
+  const int tiles_n = (a.N + BN - 1) / BN, tiles_m = (a.M + BM - 1) / BM;
+  const int tiles = tiles_m * tiles_n;
+  int w = blockIdx.x;
+  const int part = w / tiles;
+  w -= part * tiles;
+  if ((tiles & 7) == 0) w = (w & 7) * (tiles >> 3) + (w >> 3);  // contiguous band per XCD
+  constexpr int GROUP_M = 8;
+  const int group = w / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int in_group = w - group * GROUP_M * tiles_n;
+  const int m0 = (first_m + in_group % gsz) * BM, n0 = (in_group / gsz) * BN;
 
   const int u0 = (int)((int64_t)part * a.n_units / a.k_parts);
   const int u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
@@ -69,22 +97,31 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
   const size_t a_row_bytes = (size_t)a.K * ESZ;
 
   uint4 ra[A_PER], rb[B_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) ra[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) rb[i] = make_uint4(0, 0, 0, 0);
   // scale (and zero) of this lane's weight column for each n-subtile of the
   // wave, for the stage being staged: half2 (s, s) and (z, z)
   uint32_t rs[WTN], rz[WTN];
+#pragma unroll
+  for (int j = 0; j < WTN; ++j) { rs[j] = 0x3C003C00u; rz[j] = 0; }
 
+  // Stage loads are branch-free: a superblock past the part's end (only in a
+  // partial last stage) is clamped to the last one and never consumed, so the
+  // compiler sees a fixed number of loads and never drains them early.
   auto g_load = [&](int st) {
     const int kbs = kb0 + st * KSTEP;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
       const int c = tid + i * NT;
       if (A_CHUNKS % NT == 0 || c < A_CHUNKS) {
-        const int r = c >> 4, c16 = c & 15;
+        const int r = c / CPR, cc = c % CPR;
         const int row = min(m0 + r, a.M - 1);
-        const int kk = (c16 * 16) / (KB * ESZ);  // superblock of this chunk within the stage
-        if (kbs + kk < kb1)
-          ra[i] = *reinterpret_cast<const uint4*>(Ab + (size_t)row * a_row_bytes +
-                                                  (size_t)kbs * KB * ESZ + c16 * 16);
+        const int kk = (cc * 16) / (KB * ESZ);  // superblock of this chunk within the stage
+        const int kbl = min(kbs + kk, kb1 - 1);
+        ra[i] = *reinterpret_cast<const uint4*>(Ab + (size_t)row * a_row_bytes + (size_t)kbl * KB * ESZ +
+                                                (cc * 16) % (KB * ESZ));
       }
     }
 #pragma unroll
@@ -93,8 +130,8 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
       if (B_CHUNKS % NT == 0 || c < B_CHUNKS) {
         const int sbi = c >> 6, piece = c & 63;
         const int kk = sbi / NBT, nbl = sbi % NBT;
-        if (kbs + kk < kb1)
-          rb[i] = a.W[((size_t)(kbs + kk) * a.NB + (n0 >> 4) + nbl) * 64 + piece];
+        const int kbl = min(kbs + kk, kb1 - 1);
+        rb[i] = a.W[((size_t)kbl * a.NB + (n0 >> 4) + nbl) * 64 + piece];
       }
     }
     if constexpr (FMT == FMT_I4 || FMT == FMT_U4) {
@@ -121,7 +158,7 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
     for (int i = 0; i < A_PER; ++i) {
       const int c = tid + i * NT;
       if (A_CHUNKS % NT == 0 || c < A_CHUNKS)
-        *reinterpret_cast<uint4*>(&lds_a[buf][(c >> 4) * PITCH + (c & 15) * 16]) = ra[i];
+        *reinterpret_cast<uint4*>(&lds_a[buf][(c / CPR) * PITCH + (c % CPR) * 16]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
@@ -149,9 +186,10 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
     const int buf = st & 1;
     if (st + 1 < nst) g_load(st + 1);
     const int kbs = kb0 + st * KSTEP;
+    const int kvalid = min(KSTEP, kb1 - kbs);  // superblocks of this stage inside the part
 #pragma unroll
     for (int kk = 0; kk < KSTEP; ++kk) {
-      if (kbs + kk >= kb1) break;
+      if (KSTEP > 1 && kk >= kvalid) break;
       uint4 bp[WTN];
 #pragma unroll
       for (int j = 0; j < WTN; ++j)
@@ -183,8 +221,10 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
           } else if constexpr (FMT == FMT_I2) {
             uint32_t o[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
+            for (int jj = 0; jj < 3; ++jj)  // offset-binary classes: 0,1,2,3 -> -2,-1,0,1
               o[jj] = __builtin_amdgcn_perm(0u, 0x0100FFFEu, (wd >> (2 * jj)) & 0x03030303u);
+            // two's complement class: 0,1,2,3 -> 0,1,-2,-1
+            o[3] = __builtin_amdgcn_perm(0u, 0xFFFE0100u, (wd >> 6) & 0x03030303u);
             bf[j] = make_uint4(o[0], o[1], o[2], o[3]);
           } else {
             bf[j] = bp[j];
@@ -240,28 +280,31 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
 
 template <int FMT, int BM, int BN, int WM, int WN>
 hipError_t launch_t(const RunArgs& a, hipStream_t st) {
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, a.k_parts), block(WM * WN * 64);
-  hipLaunchKernelGGL((mfma_kernel<FMT, BM, BN, WM, WN>), grid, block, 0, st, a);
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((mfma_kernel<FMT, BM, BN, WM, WN>), dim3(tiles * a.k_parts), dim3(WM * WN * 64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t launch_fmt(int tile, const RunArgs& a, hipStream_t st) {
+  constexpr int BIG_N = (FMT == FMT_F16 || FMT == FMT_I8) ? 256 : 128;
   switch (tile) {
     case TILE_32x64: return launch_t<FMT, 32, 64, 2, 2>(a, st);
     case TILE_64x64: return launch_t<FMT, 64, 64, 2, 2>(a, st);
     case TILE_128x128: return launch_t<FMT, 128, 128, 2, 2>(a, st);
+    case TILE_BIG: return launch_t<FMT, 256, BIG_N, 2, 4>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-void tile_dims(int tile, int* bm, int* bn) {
+void tile_dims(int fmt, int tile, int* bm, int* bn) {
   switch (tile) {
     case TILE_32x64: *bm = 32; *bn = 64; return;
     case TILE_64x64: *bm = 64; *bn = 64; return;
-    default: *bm = 128; *bn = 128; return;
+    case TILE_128x128: *bm = 128; *bn = 128; return;
+    default: *bm = 256; *bn = (fmt == FMT_F16 || fmt == FMT_I8) ? 256 : 128; return;
   }
 }
 

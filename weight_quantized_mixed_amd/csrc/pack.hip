@@ -45,7 +45,10 @@ __global__ void pack_weights_kernel(int fmt, const void* __restrict__ w, uint4* 
         for (int t = 0; t < 4; ++t) {
           uint32_t acc = 0;
           for (int e = 0; e < 16; ++e) {
-            const uint32_t c = ((in[t] >> (2 * e)) & 0x3u) ^ 0x2u;  // offset-binary (q + 2)
+            // crumb classes 0..2 offset-binary (q + 2), class 3 (the top bits of
+            // each byte) two's complement
+            uint32_t c = (in[t] >> (2 * e)) & 0x3u;
+            if ((e >> 2) < 3) c ^= 0x2u;
             acc |= c << (8 * (e & 3) + 2 * (e >> 2));
           }
           o[t] = acc;

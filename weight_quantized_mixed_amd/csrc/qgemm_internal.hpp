@@ -16,8 +16,10 @@
 //         (q + 8 for signed, q for unsigned), so (w >> 4j) & 0x000F000F,
 //         or-ed with 0x6400 per half, is the fp16 pair (1024 + s[2j], 1024 + s[2j+1]).
 //   int2  4 words x 16 values; word t holds positions 16t..16t+15, value e in
-//         byte e%4 at bit 2*(e/4), stored offset-binary q + 2, so
-//         (w >> 2j) & 0x03030303 gives the four consecutive positions 4j..4j+3.
+//         byte e%4 at bit 2*(e/4), so (w >> 2j) & 0x03030303 gives the four
+//         consecutive positions 4j..4j+3.  Classes j = 0..2 are stored
+//         offset-binary (q + 2); class 3 (bits 6..7 of each byte) is stored two's
+//         complement, so w & 0xC0C0C0C0 reads as the signed bytes 64q.
 //   int8  16 bytes = 16 consecutive positions.
 //   fp16  8 halves = 8 consecutive positions.
 // After the weights (256-byte aligned) come the scales as [G][Npad] fp16, or
@@ -77,6 +79,7 @@ struct RunArgs {
   int32_t unit_kb;      // superblocks per split unit
   int32_t n_units;      // nkb / unit_kb
   int32_t waves;        // GEMV: waves per workgroup (K split inside the workgroup)
+  int32_t sb_per_group; // superblocks per scale group (nkb when one group spans K)
 };
 
 // kernel launchers (return hipSuccess or the launch error)
@@ -87,8 +90,19 @@ hipError_t launch_mfma(int fmt, int tile, const RunArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st);
 
+// GEMV tuning: most waves per workgroup (they split the workgroup's K range)
+// and superblocks per register stage
+#ifndef QG_GEMV_MAX_WAVES
+#define QG_GEMV_MAX_WAVES 8
+#endif
+#ifndef QG_GEMV_UNR
+#define QG_GEMV_UNR 2
+#endif
+constexpr int GEMV_MAX_WAVES = QG_GEMV_MAX_WAVES;
+
 // MFMA tile configurations (BM x BN, waves WM x WN)
-enum Tile : int { TILE_32x64 = 0, TILE_64x64 = 1, TILE_128x128 = 2, TILE_COUNT = 3 };
-void tile_dims(int tile, int* bm, int* bn);
+// TILE_BIG is 256 x 256 for fp16 / int8 weights and 256 x 128 for int4 / int2
+enum Tile : int { TILE_32x64 = 0, TILE_64x64 = 1, TILE_128x128 = 2, TILE_BIG = 3 };
+void tile_dims(int fmt, int tile, int* bm, int* bn);
 
 }  // namespace qg

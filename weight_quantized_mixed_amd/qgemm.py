@@ -39,6 +39,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # Device buffers and streams come from PyTorch, so libqgemm must bind to the
+    # HIP runtime torch already loaded (torch ships its own libamdhip64); loading
+    # libqgemm first would bring in a second runtime that cannot use torch's streams.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the binding is still usable from C pointers
+        pass
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is missing: build it with `python -m weight_quantized_mixed_amd.build`")
