@@ -153,6 +153,29 @@ GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128
            {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}])
 
 
+HEADLINE_PROFILE = os.path.join(ROOT, "profiles", "gemv_w4a16_m1_n16384_k16384.md")
+HEADLINE_SOURCES = [os.path.join(ROOT, "weight_quantized_mixed_amd", "csrc", f)
+                    for f in ("gemv.hip", "qgemm_internal.hpp")]
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE profile of the
+    headline kernel, or None when the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        h = hashlib.sha256(b"".join(open(f, "rb").read() for f in HEADLINE_SOURCES)).hexdigest()[:16]
+        fields = {}
+        for line in open(HEADLINE_PROFILE):
+            k, _, v = line.strip().partition(":")
+            if k in ("traffic_bytes_per_launch", "source_hash"):
+                fields[k] = v.strip()
+        if fields.get("source_hash") == h:
+            return int(fields["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
 def cpu_baseline(c, seed):
     """The CPU oracle, as it stands, on the benchmark workload (one full step)."""
     import numpy as np
@@ -183,6 +206,8 @@ def main():
     ap.add_argument("--no-grid", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="substring filter on grid entries")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path does not "
@@ -195,6 +220,15 @@ def main():
         sys.exit(1)
     import synth
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 18   # float32 elements
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}))
+        return
 
     head = {"w": "i4", "M": 1, "N": 16384, "K": 16384, "g": 128}
     print(f"[bench] workload {label(head)}", file=sys.stderr, flush=True)
@@ -215,7 +249,7 @@ def main():
                    "K": 16384, "group_size": 128, "k_parts": 1, "ring_copies": len(hb.packed),
                    "us_per_call": round(t_call * 1e6, 3)},
         "roofline": {"bound": bound, "achieved": round(achieved / 1e9, 2), "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": round(frac, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(frac, 4), "traffic": recorded_traffic(),
                      "alg_bytes_per_launch": hb.bytes, "kernel": "gemv_kernel<FMT_I4, 1>"},
     }
     hb.close()
