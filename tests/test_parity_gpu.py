@@ -144,3 +144,30 @@ def test_shared_blob_across_plans():
     out = c2.q.run(c2.A, c1.packed)
     torch.cuda.synchronize()
     assert_matches(out.cpu().numpy(), c2.reference(), "shared blob")
+
+
+# ---------------------------------------------------------------- 256 x 256 tile path (large M)
+BIG = [
+    # M, N, K, w_dtype, g, zeros   (>= 256 workgroups of 256 x 256, ragged M and N)
+    (4100, 4104, 512, "f16", 0, False),
+    (4096, 4100, 512, "i8", 0, False),
+    (4097, 4096, 768, "i2", 0, False),
+    (4096, 4104, 512, "i4", 128, False),
+    (4100, 4096, 512, "u4", 128, True),
+    (4096, 4096, 512, "u4", 256, False),
+    (4096, 4096, 384, "i4", -1, False),
+    (4096, 4096, 256, "i4", 0, False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,w_dtype,g,zeros", BIG)
+@pytest.mark.parametrize("kp,det", [(1, False), (2, False), (2, True)])
+def test_big_tile_parity(M, N, K, w_dtype, g, zeros, kp, det):
+    say(f"big M={M} N={N} K={K} {w_dtype} g={g} zeros={zeros} kp={kp} det={det}")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=M + N + K + kp)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([rng.choice(M, 300, replace=False), [0, 255, 256, M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(N, 300, replace=False), [0, 255, 256, N - 1]]))
+    gpu = c.run()
+    assert_matches(gpu[np.ix_(rows, cols)], c.reference(rows=rows, cols=cols),
+                   f"big {w_dtype} M={M} N={N} kp={kp}")

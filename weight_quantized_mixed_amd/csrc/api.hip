@@ -208,7 +208,9 @@ qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed
   if (a.out_mode == OUT_ATOMIC)
     e = launch_fill_zero(out_f16 ? workspace : C, (size_t)plan->M * plan->N * 4, st);
   if (e == hipSuccess)
-    e = plan->path == QGEMM_PATH_GEMV ? launch_gemv(plan->L.fmt, a, st) : launch_mfma(plan->L.fmt, plan->tile, a, st);
+    e = plan->path == QGEMM_PATH_GEMV ? launch_gemv(plan->L.fmt, a, st)
+        : (plan->tile == TILE_BIG && big_tile_supported(plan->L.fmt, a)) ? launch_mfma_big(plan->L.fmt, a, st)
+        : launch_mfma(plan->L.fmt, plan->tile, a, st);
   if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))
     e = launch_finalize(a, out_f16, st);
   return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_DEVICE;

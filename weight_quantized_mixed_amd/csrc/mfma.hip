@@ -304,7 +304,7 @@ void tile_dims(int fmt, int tile, int* bm, int* bn) {
     case TILE_32x64: *bm = 32; *bn = 64; return;
     case TILE_64x64: *bm = 64; *bn = 64; return;
     case TILE_128x128: *bm = 128; *bn = 128; return;
-    default: *bm = 256; *bn = (fmt == FMT_F16 || fmt == FMT_I8) ? 256 : 128; return;
+    default: *bm = 256; *bn = 256; return;
   }
 }
 
