@@ -21,6 +21,13 @@
 // traversal point of the mKernel AG-GEMM PR #41 discussion).
 #include "qgemm_internal.hpp"
 
+#ifndef QG_BIG_WM
+#define QG_BIG_WM 2
+#endif
+#ifndef QG_BIG_WN
+#define QG_BIG_WN 4
+#endif
+
 namespace qg {
 namespace {
 
@@ -85,14 +92,14 @@ __device__ __forceinline__ int swz(int r, int c) {
   else return c ^ ((r ^ (r >> 3)) & 7);
 }
 
-template <int FMT, bool SCALED, bool ZEROS>
-__global__ __launch_bounds__(512) void mfma_big_kernel(RunArgs a) {
+template <int FMT, bool SCALED, bool ZEROS, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void mfma_big_kernel(RunArgs a) {
   using C = BigCfg<FMT>;
   constexpr bool FP = (FMT == FMT_F16 || FMT == FMT_I4 || FMT == FMT_U4);
   constexpr bool I4 = (FMT == FMT_I4 || FMT == FMT_U4);
   constexpr bool HALF = I4 || FMT == FMT_I2;  // stage = half a superblock, two MFMA steps
-  constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NT = 512;
-  constexpr int WTM = BM / WM / 16, WTN = BN / WN / 16;  // 8 x 4 sub-tiles of 16 x 16 per wave
+  constexpr int BM = 256, BN = 256, NT = WM * WN * 64;
+  constexpr int WTM = BM / WM / 16, WTN = BN / WN / 16;  // 16 x 16 sub-tiles per wave
   constexpr int SPOS = C::SPOS, ROWB = C::ROWB, BSB = C::BSB, NSTAGE = C::NSTAGE;
   constexpr int KB = kb_of(FMT);
   constexpr int ESZ = FP ? 2 : 1;
@@ -327,7 +334,8 @@ hipError_t launch_big_t(const RunArgs& a, hipStream_t st) {
   constexpr int STAGE_BYTES = 256 * C::ROWB + 16 * C::BSB + (SCALED ? 1024 : 0);
   static_assert((size_t)STAGE_BYTES * C::NSTAGE <= 160 * 1024, "LDS budget");
   const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  hipLaunchKernelGGL((mfma_big_kernel<FMT, SCALED, ZEROS>), dim3(tiles * a.k_parts), dim3(512), 0, st, a);
+  hipLaunchKernelGGL((mfma_big_kernel<FMT, SCALED, ZEROS, QG_BIG_WM, QG_BIG_WN>), dim3(tiles * a.k_parts),
+                     dim3(QG_BIG_WM * QG_BIG_WN * 64), 0, st, a);
   return hipGetLastError();
 }
 
