@@ -1,8 +1,8 @@
 // Skinny-M path (M <= 8): wavefront dot products straight from HBM, no matrix cores.
 //
 // Each workgroup owns 64 output columns (four 16-column superblock columns)
-// and one k-part; its waves split the part's superblocks into contiguous runs
-// and meet in LDS at the end (the intra-workgroup "block reduction" that the
+// and one k-part; its waves take the part's superblock rows in turn and meet
+// in LDS at the end (the intra-workgroup "block reduction" that the
 // BitBLAS issue #252 discussion names as the cure for slow skinny dequantised
 // shapes).  Lane l owns column n = 64*rb + l: for every superblock it loads
 // the four 16-byte pieces of its column (one wave-wide load per quarter reads
@@ -100,9 +100,12 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
   const int u0 = (int)((int64_t)part * a.n_units / a.k_parts);
   const int u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
   const int kb0 = u0 * a.unit_kb, kb1 = u1 * a.unit_kb;
-  const int per = (kb1 - kb0 + a.waves - 1) / a.waves;
-  const int my0 = min(kb0 + wave * per, kb1);
-  const int my1 = min(my0 + per, kb1);
+  // The waves of a workgroup take the part's superblock rows in turn (wave w:
+  // rows kb0 + w, kb0 + w + waves, ...), so at any moment the whole grid streams
+  // one narrow band of consecutive 1 KiB superblock rows, which the memory system
+  // serves much faster than one contiguous run per wave spread over the matrix.
+  const int cnt = kb1 - kb0 > wave ? (kb1 - kb0 - wave + a.waves - 1) / a.waves : 0;  // rows of this wave
+  auto row_of = [&](int j) { return kb0 + wave + j * a.waves; };
 
   cptr A = (cptr)a.A;
   const uint32_t* __restrict__ Av = static_cast<const uint32_t*>(a.A);
@@ -127,10 +130,10 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
   // Every stage issues the same loads (superblocks past the wave's range re-read
   // its last one and are not used), so the compiler can count outstanding loads
   // exactly and never has to drain the next stage to use this one.
-  auto load = [&](Stage& s, int kb) {
+  auto load = [&](Stage& s, int j) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const uint32_t kbl = (uint32_t)min(kb + u, my1 - 1);
+      const uint32_t kbl = (uint32_t)row_of(min(j + u, cnt - 1));
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) s.w[u][kq] = stream_load(&Wl[kbl * sb_stride + kq * 16]);
       if constexpr (FOLD) {
@@ -294,22 +297,184 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
     }
   };
 
+  // Several activation rows: the superblock's activations stream through the
+  // scalar unit in 16-dword chunks (one piece of one row at a time), and each
+  // chunk is requested right after the previous one has landed, so at most two
+  // chunks occupy scalar registers whatever the number of rows (loading a whole
+  // superblock for every row at once would overflow them).  Scalar loads can
+  // complete out of order, hence the full lgkmcnt wait before each request.
+  auto do_block_rows = [&](const uint4 (&wv)[4], const uint32_t (&as)[MR], uint32_t sc, int kb) {
+    constexpr int NC = (FMT == FMT_F16 || FMT == FMT_I8) ? 1 : 4;  // chunks per row and superblock
+    struct Chunk { uint32_t d[16]; };
+    auto fetch = [&](int c, int m) {
+      Chunk ch;
+      uint32_t off = __builtin_amdgcn_readfirstlane(m * a_row + kb * A_DW_SB + c * 16);  // uniform
+      // constant-space loads count as invariant and could be hoisted past the
+      // wait below; passing the offset through an (empty) volatile asm pins
+      // the request after it
+      asm volatile("; chunk %0" : "+s"(off));
+      cptr p = A + off;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ch.d[i] = p[i];
+      return ch;
+    };
+    // runs body(c, m, chunk) over every (piece c, row m), prep(c) before the rows of piece c
+    auto sweep = [&](auto&& prep, auto&& body) {
+      Chunk cur = fetch(0, 0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        prep(c);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): cur has landed
+          const bool more = !(c == NC - 1 && m == MR - 1);
+          Chunk nxt;
+          if (more) nxt = fetch(m == MR - 1 ? c + 1 : c, m == MR - 1 ? 0 : m + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          body(c, m, cur);
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) cur = nxt;
+        }
+      }
+    };
+
+    if constexpr (I4 && FOLD) {
+      const uint32_t MASK_E = 0x000F000Fu, MASK_O = 0x00F000F0u, EXP16 = 0x64006400u;
+      float accE[MR], accO[MR];
+#pragma unroll
+      for (int m = 0; m < MR; ++m) { accE[m] = 0.f; accO[m] = 0.f; }
+      half2v e0[4], o0[4], e1[4], o1[4];
+      sweep(
+          [&](int c) {
+            const uint32_t wd[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t w = wd[t], w8 = w >> 8;
+              e0[t] = as_h2(and_or(w, MASK_E, EXP16));
+              o0[t] = as_h2(and_or(w, MASK_O, EXP16));
+              e1[t] = as_h2(and_or(w8, MASK_E, EXP16));
+              o1[t] = as_h2(and_or(w8, MASK_O, EXP16));
+            }
+          },
+          [&](int c, int m, const Chunk& ch) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              accE[m] = __builtin_amdgcn_fdot2(e0[t], as_h2(ch.d[4 * t + 0]), accE[m], false);
+              accO[m] = __builtin_amdgcn_fdot2(o0[t], as_h2(ch.d[4 * t + 1]), accO[m], false);
+              accE[m] = __builtin_amdgcn_fdot2(e1[t], as_h2(ch.d[4 * t + 2]), accE[m], false);
+              accO[m] = __builtin_amdgcn_fdot2(o1[t], as_h2(ch.d[4 * t + 3]), accO[m], false);
+            }
+          });
+      constexpr float cE = (FMT == FMT_I4) ? 1032.f : 1024.f, cO = (FMT == FMT_I4) ? 72.f : 64.f;
+      const float s = h2f((uint16_t)(sc & 0xFFFFu)), z = h2f((uint16_t)(sc >> 16));
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const float h = half_wave_sums(__builtin_amdgcn_fdot2(as_h2(as[m]), as_h2(0x3C003C00u), 0.f, false));
+        const float SE = lane_value(h, 31), SO = lane_value(h, 63);
+        float v = accE[m] + accO[m] * 0.0625f - cE * SE - cO * SO;
+        if constexpr (ZEROS) v -= z * (SE + SO);
+        tot[m] += SCALED ? s * v : v;
+      }
+    } else if constexpr (I4) {
+      constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;  // 1032 or 1024
+      const half2v hb = as_h2(bias);
+      half2v qv[4][4];
+      float gsv[4], gzv[4];  // scale (and zero point) of each piece's group
+#pragma unroll
+      for (int c = 0; c < 4; ++c) scale_of((kb * 128 + c * 32) / a.group_size, gsv[c], gzv[c]);
+      float pq[MR], pa[MR];
+      sweep(
+          [&](int c) {
+            const uint32_t wd[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) qv[t][j] = as_h2(((wd[t] >> (4 * j)) & 0x000F000Fu) | 0x64006400u) - hb;
+          },
+          [&](int c, int m, const Chunk& ch) {
+            pq[m] = 0.f;
+            pa[m] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                pq[m] = __builtin_amdgcn_fdot2(qv[t][j], as_h2(ch.d[4 * t + j]), pq[m], false);
+                if (FMT == FMT_U4 && a.zeros)
+                  pa[m] = __builtin_amdgcn_fdot2(as_h2(0x3C003C00u), as_h2(ch.d[4 * t + j]), pa[m], false);
+              }
+            tot[m] += gsv[c] * (pq[m] - gzv[c] * pa[m]);
+          });
+    } else if constexpr (FMT == FMT_F16 || FMT == FMT_I8) {
+      sweep([](int) {},
+            [&](int, int m, const Chunk& ch) {
+#pragma unroll
+              for (int kq = 0; kq < 4; ++kq) {
+                const uint32_t wd[4] = {wv[kq].x, wv[kq].y, wv[kq].z, wv[kq].w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  if constexpr (FMT == FMT_F16)
+                    tot[m] = __builtin_amdgcn_fdot2(as_h2(wd[t]), as_h2(ch.d[kq * 4 + t]), tot[m], false);
+                  else
+                    tot[m] = __builtin_amdgcn_sdot4((int)wd[t], (int)ch.d[kq * 4 + t], tot[m], false);
+                }
+              }
+            });
+    } else {  // FMT_I2
+      int acc[4][MR];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[j][m] = 0;
+      int q[4][4];
+      sweep(
+          [&](int c) {
+            const uint32_t wd[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              q[t][0] = (int)(wd[t] & 0x03030303u);
+              q[t][1] = (int)(wd[t] & 0x0C0C0C0Cu);
+              q[t][2] = (int)(wd[t] & 0x30303030u);
+              q[t][3] = (int)(wd[t] & 0xC0C0C0C0u);
+            }
+          },
+          [&](int, int m, const Chunk& ch) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                acc[j][m] = __builtin_amdgcn_sdot4(q[t][j], (int)ch.d[4 * t + j], acc[j][m], false);
+          });
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const int mine = (lane & 3) == 3 ? 0 : __builtin_amdgcn_sdot4((int)as[m], 0x01010101, 0, false);
+        const int h = half_wave_sums(mine);
+        const int S012 = lane_value(h, 31) + lane_value(h, 63);
+        tot[m] += acc[0][m] + (acc[1][m] >> 2) + (acc[2][m] >> 4) + (acc[3][m] >> 6) - 2 * S012;
+      }
+    }
+  };
+
+  auto block = [&](const uint4 (&wv)[4], const uint32_t (&as)[MR], uint32_t sc, int kb) {
+    if constexpr (MR == 1) do_block(wv, as, sc, kb);
+    else do_block_rows(wv, as, sc, kb);
+  };
+
   // two register stages: loads of the next UNR superblocks fly while these are consumed
   Stage s0, s1;
-  int kb = my0;
-  if (kb < my1) load(s0, kb);
-  while (kb < my1) {
-    load(s1, kb + UNR);
+  int j = 0;
+  if (j < cnt) load(s0, j);
+  while (j < cnt) {
+    load(s1, j + UNR);
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
-      if (kb + u < my1) do_block(s0.w[u], s0.as[u], s0.sc[u], kb + u);
-    kb += UNR;
-    if (kb >= my1) break;
-    load(s0, kb + UNR);
+      if (j + u < cnt) block(s0.w[u], s0.as[u], s0.sc[u], row_of(j + u));
+    j += UNR;
+    if (j >= cnt) break;
+    load(s0, j + UNR);
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
-      if (kb + u < my1) do_block(s1.w[u], s1.as[u], s1.sc[u], kb + u);
-    kb += UNR;
+      if (j + u < cnt) block(s1.w[u], s1.as[u], s1.sc[u], row_of(j + u));
+    j += UNR;
   }
 
   // block reduction across the waves of the workgroup

@@ -47,6 +47,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -85,9 +92,13 @@ template <> struct BigCfg<FMT_I4> { static constexpr int SPOS = 64, ROWB = 128, 
 template <> struct BigCfg<FMT_U4> { static constexpr int SPOS = 64, ROWB = 128, BSB = 512, NSTAGE = 3; };
 template <> struct BigCfg<FMT_I2> { static constexpr int SPOS = 128, ROWB = 128, BSB = 512, NSTAGE = 3; };
 
-// position (in 16-byte units) of chunk c of activation row r
+// position (in 16-byte units) of chunk c of activation row r.  Only r mod 16
+// enters, so rows that are 16 apart share one pattern and a fragment read's lane
+// addresses differ between sub-tiles by a constant offset; any 16 consecutive rows
+// (and any 8 aligned ones) spread over distinct 16-byte bank groups.
 template <int ROWB>
 __device__ __forceinline__ int swz(int r, int c) {
+  r &= 15;
   if constexpr (ROWB == 64) return c ^ (((r >> 1) ^ (r >> 2)) & 3);
   else return c ^ ((r ^ (r >> 3)) & 7);
 }
@@ -200,104 +211,159 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_big_kernel(RunArgs a) {
 #pragma unroll
     for (int j = 0; j < WTN; ++j) acc[i][j] = acc_v{0, 0, 0, 0};
 
-  // prologue: NSTAGE - 1 stages in flight
-#pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st) issue(st);
+  // Register double buffering: the fragments of the next MFMA step are read from
+  // LDS (and, for int4 / int2, upcast) while the MFMAs of the current step run, so
+  // LDS reads, dequantisation and matrix-core work overlap instead of alternating.
+  struct Frag {
+    uint4 a[WTM];  // activation fragments (16 rows each)
+    uint4 b[WTN];  // MFMA-ready weight fragments (16 columns each)
+  };
+  // int4 / int2: the one packed word (8 int4 or 16 int2 values) that a lane feeds
+  // to an MFMA step, per column block, and the block's scale / zero point pair
+  uint32_t rw[WTN];
+  uint32_t sc[WTN], zc[WTN];
 
-  for (int st = 0; st < nst; ++st) {
-    // this wave's loads of stage st are done when at most (NSTAGE - 2) stages of
-    // loads remain outstanding; the barrier makes every wave's loads visible and
-    // frees the slot that the next issue overwrites (read in the previous step).
-    // A bare s_barrier (a compiler memory barrier through the clobber) instead of
-    // __syncthreads, whose fence would drain the loads still in flight.
-    if (SCALED && wave == 0) wait_vmcnt<(NSTAGE - 2) * (LOADS + 1)>();
-    else wait_vmcnt<(NSTAGE - 2) * LOADS>();
+  auto slot = [&](int s) -> const uint8_t* { return lds + (s % NSTAGE) * STAGE_BYTES; };
+
+  // stage sn becomes readable: this wave's loads of it are done when at most
+  // NSTAGE - 2 later stages of loads are outstanding, and lgkmcnt(0) retires this
+  // wave's LDS reads of the stage held in registers, whose ring slot the load
+  // issued after the barrier overwrites.  A bare s_barrier (a compiler memory
+  // barrier through the clobber) instead of __syncthreads, whose fence would
+  // drain the loads still in flight.
+  auto sync_stage = [&](int sn) {
+    if (SCALED && wave == 0) wait_vm_lgkm0<(NSTAGE - 2) * (LOADS + 1)>();
+    else wait_vm_lgkm0<(NSTAGE - 2) * LOADS>();
     asm volatile("s_barrier" ::: "memory");
-    issue(st + NSTAGE - 1);
+    issue(sn + NSTAGE - 1);
+  };
 
-    const uint8_t* base = lds + (st % NSTAGE) * STAGE_BYTES;
-    const uint8_t* la = base;
-    const uint8_t* lb = base + A_BYTES;
+  // keeps the machine scheduler from moving instructions across it, so that the
+  // reads of the next fragments issue before the MFMAs of the current ones and no
+  // MFMA of the next step is hoisted above the barrier that guards its data
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-    // weight fragments of this wave's 4 column blocks (and their scales)
-    uint4 bp[WTN];
-    uint32_t sc[WTN], zc[WTN];
+  // fragments of step t of stage s: activation rows, and the weight pieces of this
+  // wave's column blocks (straight into the fragment for fp16 / int8; for int4 /
+  // int2 the packed word, plus the stage's scales on its first step)
+  auto read_step = [&](Frag& f, int s, int t) {
+    const uint8_t* base = slot(s);
+    int chunk;
+    if constexpr (HALF) chunk = (q & 1) * 4 + (2 * t + (q >> 1));  // piece q & 1, word 2t + (q >> 1)
+    else chunk = q;                                                  // 8 fp16 / 16 int8 per lane group
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      const int r = (wm * WTM + i) * 16 + l16;
+      f.a[i] = *reinterpret_cast<const uint4*>(base + r * ROWB + swz<ROWB>(r, chunk) * 16);
+    }
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
-      const int nbl = wn * WTN + j;
-      int off;
-      if constexpr (HALF) off = ((q & 1) * 16 + l16) * 16;  // piece 2h + (q & 1) of the half superblock
-      else off = lane * 16;                                // whole superblock, piece = lane
-      bp[j] = *reinterpret_cast<const uint4*>(lb + nbl * BSB + off);
+      const uint8_t* lb = base + A_BYTES + (wn * WTN + j) * BSB;
+      if constexpr (HALF)
+        rw[j] = *reinterpret_cast<const uint32_t*>(lb + ((q & 1) * 16 + l16) * 16 + (2 * t + (q >> 1)) * 4);
+      else
+        f.b[j] = *reinterpret_cast<const uint4*>(lb + lane * 16);  // whole superblock, piece = lane
       if constexpr (SCALED) {
-        const int col = nbl * 16 + l16;
-        if constexpr (ZEROS) {
-          const uint32_t v = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4);
-          sc[j] = (v & 0xFFFFu) * 0x10001u;
-          zc[j] = (v >> 16) * 0x10001u;
-        } else {
-          const uint32_t v = *reinterpret_cast<const uint16_t*>(base + A_BYTES + B_BYTES + col * 2);
-          sc[j] = v * 0x10001u;
-          zc[j] = 0;
-        }
-      }
-    }
-
-    // MFMA steps of this stage: fp16 1 (32 positions), int8 1 (64), int4 2 (2 x 32), int2 2 (2 x 64)
-    constexpr int NSTEP = HALF ? 2 : 1;
-#pragma unroll
-    for (int t = 0; t < NSTEP; ++t) {
-      // activation fragment position (16-byte chunk) of lane group q in this stage
-      int chunk;
-      if constexpr (HALF) chunk = (q & 1) * 4 + (2 * t + (q >> 1));  // piece q & 1, word 2t + (q >> 1)
-      else chunk = q;                                                  // 8 fp16 / 16 int8 per lane group
-      uint4 af[WTM];
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        const int r = (wm * WTM + i) * 16 + l16;
-        af[i] = *reinterpret_cast<const uint4*>(la + r * ROWB + swz<ROWB>(r, chunk) * 16);
-      }
-      // column block by column block: the upcast of block j + 1 can issue while the
-      // MFMAs of block j run
-#pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        uint4 bf;
-        if constexpr (I4) {
-          const int word = 2 * t + (q >> 1);
-          const uint32_t wd = word == 0 ? bp[j].x : word == 1 ? bp[j].y : word == 2 ? bp[j].z : bp[j].w;
-          constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;
-          uint32_t o[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            half2v v = as_h2(and_or(wd >> (4 * jj), 0x000F000Fu, 0x64006400u)) - as_h2(bias);
-            if constexpr (ZEROS) v = v - as_h2(zc[j]);
-            if constexpr (SCALED) v = v * as_h2(sc[j]);
-            o[jj] = as_u32(v);
+        if (t == 0) {
+          const int col = (wn * WTN + j) * 16 + l16;
+          if constexpr (ZEROS) {
+            const uint32_t u = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4);
+            sc[j] = (u & 0xFFFFu) * 0x10001u;
+            zc[j] = (u >> 16) * 0x10001u;
+          } else {
+            const uint32_t u = *reinterpret_cast<const uint16_t*>(base + A_BYTES + B_BYTES + col * 2);
+            sc[j] = u * 0x10001u;
+            zc[j] = 0;
           }
-          bf = make_uint4(o[0], o[1], o[2], o[3]);
-        } else if constexpr (FMT == FMT_I2) {
-          const int word = 2 * t + (q >> 1);
-          const uint32_t wd = word == 0 ? bp[j].x : word == 1 ? bp[j].y : word == 2 ? bp[j].z : bp[j].w;
-          uint32_t o[4];
-#pragma unroll
-          for (int jj = 0; jj < 3; ++jj)
-            o[jj] = __builtin_amdgcn_perm(0u, 0x0100FFFEu, (wd >> (2 * jj)) & 0x03030303u);
-          o[3] = __builtin_amdgcn_perm(0u, 0xFFFE0100u, (wd >> 6) & 0x03030303u);
-          bf = make_uint4(o[0], o[1], o[2], o[3]);
-        } else {
-          bf = bp[j];
-        }
-#pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-          if constexpr (FP)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(half8v, af[i]), __builtin_bit_cast(half8v, bf), acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                __builtin_bit_cast(int4v, af[i]), __builtin_bit_cast(int4v, bf), acc[i][j], 0, 0, 0);
         }
       }
     }
+  };
+
+  // upcast of column block j from its packed word (int4 / int2 only)
+  auto make_b = [&](Frag& f, int j) {
+    if constexpr (HALF) {
+      const uint32_t wd = rw[j];
+      uint32_t o[4];
+      if constexpr (I4) {
+        constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          half2v v = as_h2(and_or(wd >> (4 * jj), 0x000F000Fu, 0x64006400u)) - as_h2(bias);
+          if constexpr (ZEROS) v = v - as_h2(zc[j]);
+          if constexpr (SCALED) v = v * as_h2(sc[j]);
+          o[jj] = as_u32(v);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 3; ++jj)
+          o[jj] = __builtin_amdgcn_perm(0u, 0x0100FFFEu, (wd >> (2 * jj)) & 0x03030303u);
+        o[3] = __builtin_amdgcn_perm(0u, 0xFFFE0100u, (wd >> 6) & 0x03030303u);
+      }
+      f.b[j] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
+  auto mma = [&](const Frag& f, int j) {
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      if constexpr (FP)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(half8v, f.a[i]), __builtin_bit_cast(half8v, f.b[j]), acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            __builtin_bit_cast(int4v, f.a[i]), __builtin_bit_cast(int4v, f.b[j]), acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // one MFMA step on cur while nxt (already read) is upcast, block by block
+  auto compute = [&](const Frag& cur, Frag& nxt) {
+    fence();
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) {
+      mma(cur, j);
+      make_b(nxt, j);
+    }
+    fence();
+  };
+
+  // prologue: NSTAGE stages in flight, then the fragments of step 0
+#pragma unroll
+  for (int st = 0; st < NSTAGE; ++st) issue(st);
+  if (SCALED && wave == 0) wait_vm_lgkm0<(NSTAGE - 1) * (LOADS + 1)>();
+  else wait_vm_lgkm0<(NSTAGE - 1) * LOADS>();
+  asm volatile("s_barrier" ::: "memory");
+
+  Frag X, Y;
+  read_step(X, 0, 0);
+#pragma unroll
+  for (int j = 0; j < WTN; ++j) make_b(X, j);
+
+  if constexpr (HALF) {
+    // two MFMA steps per stage: X holds step 0 of stage s, Y step 1
+    for (int s = 0; s < nst; ++s) {
+      fence();
+      read_step(Y, s, 1);
+      compute(X, Y);
+      sync_stage(s + 1);  // past the last stage this reads clamped copies that are never used
+      fence();
+      read_step(X, s + 1, 0);
+      compute(Y, X);
+    }
+  } else {
+    // one MFMA step per stage, two stages per iteration
+    int s = 0;
+    for (; s + 1 < nst; s += 2) {
+      sync_stage(s + 1);
+      fence();
+      read_step(Y, s + 1, 0);
+      compute(X, Y);
+      sync_stage(s + 2);
+      fence();
+      read_step(X, s + 2, 0);
+      compute(Y, X);
+    }
+    if (s < nst) compute(X, Y);
   }
   wait_vmcnt<0>();  // drain the clamped tail loads before the workgroup's LDS is released
 

@@ -99,7 +99,7 @@ hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st);
 #define QG_GEMV_MAX_WAVES 8
 #endif
 #ifndef QG_GEMV_UNR
-#define QG_GEMV_UNR 2
+#define QG_GEMV_UNR 1
 #endif
 constexpr int GEMV_MAX_WAVES = QG_GEMV_MAX_WAVES;
 
