@@ -171,3 +171,25 @@ def test_big_tile_parity(M, N, K, w_dtype, g, zeros, kp, det):
     gpu = c.run()
     assert_matches(gpu[np.ix_(rows, cols)], c.reference(rows=rows, cols=cols),
                    f"big {w_dtype} M={M} N={N} kp={kp}")
+
+
+# ---------------------------------------------------------------- direct-load tiles of every shape
+# The tile is the largest one within M's power-of-two row cap that still gives >= 256
+# workgroups (N / BN x M / BM x k_parts), so these shapes select, in order:
+# 32x64, 32x128, 32x256, 64x128, 64x256, 128x256, 256x256 (rows and columns ragged).
+DL_SHAPES = [(20, 16376, 1, False), (20, 16376, 2, True), (20, 16376, 4, False), (40, 16376, 2, False),
+             (40, 16376, 4, True), (100, 16376, 4, False), (300, 16376, 2, True)]
+DL_FORMATS = [("i4", 128, False), ("u4", 128, True), ("u4", 256, False), ("f16", 0, False), ("i8", 0, False),
+              ("i2", 0, False)]
+
+
+@pytest.mark.parametrize("M,N,kp,det", DL_SHAPES)
+@pytest.mark.parametrize("w_dtype,g,zeros", DL_FORMATS)
+def test_direct_load_tiles(M, N, kp, det, w_dtype, g, zeros):
+    K = 1024
+    say(f"dl M={M} N={N} K={K} {w_dtype} g={g} zeros={zeros} kp={kp} det={det}")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=7 * M + kp)
+    rng = np.random.default_rng(M + kp)
+    cols = np.unique(np.concatenate([rng.choice(N, 400, replace=False), [0, 63, 64, 255, 256, N - 1]]))
+    gpu = c.run()
+    assert_matches(gpu[:, cols], c.reference(cols=cols), f"dl {w_dtype} M={M} kp={kp}")

@@ -17,7 +17,8 @@ struct qgemm_plan {
   uint32_t flags;
   Layout L;
   int path;          // QGEMM_PATH_GEMV or QGEMM_PATH_MFMA
-  int tile;          // MFMA tile
+  int dl_tile;       // direct-load MFMA tile, or -1
+  int tile;          // LDS-staged MFMA tile (used when dl_tile < 0)
   int gemv_waves;    // GEMV waves per workgroup
   int32_t unit_kb, n_units;
   size_t ws_bytes;
@@ -73,7 +74,7 @@ int choose_gemv_waves(const qgemm_plan* p) {
   return (int)want;
 }
 
-// Largest tile that still gives every CU a workgroup (256 CUs).
+// LDS-staged kernel: largest tile that still gives every CU a workgroup (256 CUs).
 int choose_tile(const qgemm_plan* p) {
   if (p->M <= 32) return TILE_32x64;
   auto wgs = [&](int tile) {
@@ -171,6 +172,10 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   p->n_units = (int32_t)n_units;
   p->path = M <= 8 ? QGEMM_PATH_GEMV : QGEMM_PATH_MFMA;
   p->tile = choose_tile(p);
+  p->dl_tile = p->path == QGEMM_PATH_MFMA
+                   ? choose_dl_tile(fmt, M, N, k_parts,
+                                    group_size == 0 ? SC_NONE : (group_size > 0 && group_size < KB) ? SC_PIECE : SC_BLOCK)
+                   : -1;
   p->gemv_waves = choose_gemv_waves(p);
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   if (k_parts == 1) p->ws_bytes = 0;
@@ -209,7 +214,7 @@ qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed
     e = launch_fill_zero(out_f16 ? workspace : C, (size_t)plan->M * plan->N * 4, st);
   if (e == hipSuccess)
     e = plan->path == QGEMM_PATH_GEMV ? launch_gemv(plan->L.fmt, a, st)
-        : (plan->tile == TILE_BIG && big_tile_supported(plan->L.fmt, a)) ? launch_mfma_big(plan->L.fmt, a, st)
+        : plan->dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, plan->dl_tile, a, st)
         : launch_mfma(plan->L.fmt, plan->tile, a, st);
   if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))
     e = launch_finalize(a, out_f16, st);

@@ -1,0 +1,611 @@
+// Direct-load MFMA path (M > 8): BM x BN output tiles (32..256 rows, 64..256
+// columns) computed by 4 or 8 waves from a ring of NSTAGE LDS stages that
+// global_load_lds_dwordx4 fills straight from memory (lane l's 16 bytes land at
+// the instruction's LDS base + 16 l, so no registers or LDS-store instructions
+// carry the staging) -- the multi-stage software pipelining of hidet issue #364
+// with num_stages = NSTAGE, as deep as the 160 KiB of LDS allows for the tile.
+//
+// A stage covers SPOS reduction positions: half a superblock for int4 / int2
+// (two MFMA steps), one superblock for fp16 / int8 (one step).  Its 1 KiB
+// direct loads are dealt round-robin over the waves, and each wave waits for
+// its own count.  Each MFMA step consumes 32 (fp16) or 64 (int8) positions;
+// lane group q of a step takes piece q of the fp16 / int8 superblock, or packed
+// word 2t + (q >> 1) of piece q & 1 of the int4 / int2 half superblock, and the
+// activation fragment reads the same positions, so A and B agree on the K
+// order by construction.
+//
+// Activation rows sit unpadded in LDS with their 16-byte chunks XOR-swizzled
+// (chunk c of row r at position c ^ swz(r)), which keeps the fragment reads free
+// of bank conflicts; the swizzle is applied on the global side of the direct
+// loads.  Group scales (and zero points) of the stage ride along as one more
+// direct load into LDS.
+//
+// Register double buffering: the fragments of the next step are read from LDS
+// (and int4 / int2 upcast) while the MFMAs of the current step run.
+//
+// Small int4 / int2 tiles split K inside the workgroup: KS wave groups take
+// stages in turn and meet in LDS at the end (the intra-workgroup block
+// reduction that the BitBLAS issue #252 discussion names for skinny dequantised
+// shapes).  Each wave then covers a wide slice of the tile, so the fixed cost of
+// a stage (barrier, waits, addressing) is spread over many MFMAs, and no weight
+// is upcast twice.
+//
+// Workgroups are numbered so each XCD owns a contiguous band of tiles, swept in
+// column-major groups of 8 tile rows (L2 reuse of the shared A / B blocks, the
+// traversal point of the mKernel AG-GEMM PR #41 discussion).
+#include <type_traits>
+#include <utility>
+
+#include "qgemm_internal.hpp"
+
+namespace qg {
+namespace {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
+__device__ __forceinline__ uint32_t as_u32(half2v x) { return __builtin_bit_cast(uint32_t, x); }
+
+// s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte direct global -> LDS load of this lane (gfx950 global_load_lds_dwordx4:
+// lane l's bytes land at LDS address m0 + 16 l).  Written as inline assembly so
+// that the compiler, which cannot tell the ring slots apart, does not make every
+// later LDS read wait for all of these loads; m0 is saved and restored inside.
+// Completion is waited for explicitly (s_waitcnt vmcnt + s_barrier) before a
+// slot is read.  No register receives data from these loads.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+
+// (x & m) | c in one VALU op (masks that are not inline constants go in registers)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
+
+// position (in 16-byte units) of chunk c of activation row r.  Only r mod 16
+// enters, so rows that are 16 apart share one pattern and a fragment read's lane
+// addresses differ between sub-tiles by a constant offset; any 16 consecutive
+// rows reading one chunk spread over distinct 16-byte bank groups.
+template <int ROWB>
+__device__ __forceinline__ int swz(int r, int c) {
+  r &= 15;
+  if constexpr (ROWB == 64) return c ^ (((r >> 1) ^ (r >> 2)) & 3);
+  else if constexpr (ROWB == 128) return c ^ ((r ^ (r >> 3)) & 7);
+  else return c ^ r;
+}
+
+template <int... T, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, T...>, F&& f) {
+  (f(std::integral_constant<int, T>{}), ...);
+}
+
+#ifndef QG_DL_MAXST
+#define QG_DL_MAXST 16
+#endif
+
+// Stage geometry of a tile configuration.
+template <int FMT, int BM_, int BN_, int WM_, int WN_, int KS_, bool SCALED>
+struct Geo {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = WM * WN;  // waves of one K group
+  static constexpr int KS = KS_, NWT = NW * KS;                                // K groups, all waves
+  static constexpr bool FP = FMT != FMT_I8 && FMT != FMT_I2;  // fp16 activations
+  static constexpr bool PACKED = FMT == FMT_I4 || FMT == FMT_U4 || FMT == FMT_I2;
+  static constexpr int KB = kb_of(FMT);
+  static constexpr int ESZ = FP ? 2 : 1;
+  static constexpr int SPOS = PACKED ? KB / 2 : KB;
+  static constexpr int NSTEP = SPOS / (FP ? 32 : 64);  // MFMA steps per stage
+  static constexpr int ROWB = SPOS * ESZ;              // activation bytes per row per stage
+  static constexpr int BSB = SPOS * 1024 / KB;         // weight bytes per 16 columns per stage
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN / 16 * BSB;
+  static constexpr int S_BYTES = SCALED ? 1024 : 0;  // one direct-load slot of scales
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  // 1 KiB slots per stage, dealt round-robin over all the waves
+  static constexpr int NS_A = A_BYTES / 1024, NS_B = B_BYTES / 1024;
+  static constexpr int A_MAX = (NS_A + NWT - 1) / NWT, B_MAX = (NS_B + NWT - 1) / NWT;
+  static constexpr int LMIN = NS_A / NWT + NS_B / NWT;              // fewest loads of a wave per stage
+  static constexpr int LMAX = A_MAX + B_MAX + (SCALED ? 1 : 0);    // most (wave 0 adds the scale slot)
+  static constexpr int WTM = BM / WM / 16, WTN = BN / WN / 16;
+  // ring depth: the 256 x 256 tiles keep their measured depth, the others take
+  // as many stages as LDS (and the 6-bit load counter) allows, up to 16, in
+  // whole rounds of KS stages
+  static constexpr int fit(int n) {
+    while (n > 2 && (n * STAGE > 160 * 1024 || (n - KS) * LMAX > 63 || n % KS != 0)) --n;
+    return n;
+  }
+  static constexpr int NSTAGE = BM == 256 ? fit((FMT == FMT_F16 || FMT == FMT_I8) ? 4 : 3) : fit(QG_DL_MAXST);
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KiB slots");
+  static_assert(NSTEP == 1 || NSTEP == 2, "one or two MFMA steps per stage");
+  static_assert(ROWB == 64 || ROWB == 128, "activation row bytes");
+  static_assert(NSTAGE >= 3 * KS, "ring depth");
+  static_assert(KS == 1 || ((KS == 2 || KS == 4) && PACKED), "K groups: 2 or 4, for the two-step int4 / int2 stages");
+  static constexpr int RED = NW * WTM * WTN * 64;  // accumulator vectors of one K group
+  static_assert((KS - 1) * RED * 16 <= NSTAGE * STAGE, "K-group reduction fits in the ring");
+};
+
+// s_waitcnt vmcnt(MUL * n) lgkmcnt(0) for a wave-uniform n in [LO, HI]
+template <int LO, int HI, int MUL>
+__device__ __forceinline__ void wait_loads(int n) {
+  static_for(std::make_integer_sequence<int, HI - LO + 1>{}, [&](auto T) {
+    constexpr int v = LO + decltype(T)::value;
+    if (n == v) wait_vm_lgkm0<MUL * v>();
+  });
+}
+
+template <int FMT, class G, bool SCALED, bool ZEROS>
+__global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
+  constexpr bool FP = G::FP, PACKED = G::PACKED;
+  constexpr bool I4 = (FMT == FMT_I4 || FMT == FMT_U4);
+  constexpr int BM = G::BM, BN = G::BN, WN = G::WN, NW = G::NW, KS = G::KS, NWT = G::NWT;
+  constexpr int WTM = G::WTM, WTN = G::WTN;
+  constexpr int SPOS = G::SPOS, ROWB = G::ROWB, BSB = G::BSB, NSTAGE = G::NSTAGE, NSTEP = G::NSTEP;
+  constexpr int KB = G::KB, ESZ = G::ESZ;
+  constexpr int A_BYTES = G::A_BYTES, B_BYTES = G::B_BYTES, STAGE = G::STAGE;
+  constexpr int NS_A = G::NS_A, NS_B = G::NS_B, A_MAX = G::A_MAX, B_MAX = G::B_MAX;
+  typedef typename std::conditional<FP, float4v, int4v>::type acc_v;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave / NW, wl = wave % NW;  // K group, wave within it
+  const int wm = wl / WN, wn = wl % WN;
+  const int q = lane >> 4, l16 = lane & 15;
+
+  // ---- tile of this workgroup
+  const int tiles_n = (a.N + BN - 1) / BN, tiles_m = (a.M + BM - 1) / BM;
+  const int tiles = tiles_m * tiles_n;
+  int w = blockIdx.x;
+  const int part = w / tiles;
+  w -= part * tiles;
+  if ((tiles & 7) == 0) w = (w & 7) * (tiles >> 3) + (w >> 3);
+  constexpr int GROUP_M = 8;
+  const int group = w / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int in_group = w - group * GROUP_M * tiles_n;
+  const int m0 = (first_m + in_group % gsz) * BM, n0 = (in_group / gsz) * BN;
+
+  // ---- stages of this k-part
+  constexpr int SPB = KB / SPOS;  // stages per superblock
+  const int u0 = (int)((int64_t)part * a.n_units / a.k_parts);
+  const int u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
+  const int s0 = u0 * a.unit_kb * SPB, s1 = u1 * a.unit_kb * SPB;  // global stage indices
+  const int nst = s1 - s0;
+
+  const uint8_t* __restrict__ Ab = static_cast<const uint8_t*>(a.A);
+  const size_t a_row_bytes = (size_t)a.K * ESZ;
+  const uint8_t* __restrict__ Wb = reinterpret_cast<const uint8_t*>(a.W);
+
+  // This wave's 1 KiB slots of a stage: A slots i * NWT + wave < NS_A, then B
+  // slots likewise; wave 0 also loads the scale slot.
+  const int la = (NS_A - wave + NWT - 1) / NWT, lb = (NS_B - wave + NWT - 1) / NWT;
+  const int my_loads = la + lb + ((SCALED && wave == 0) ? 1 : 0);
+
+  // Per-lane global source of each direct load (the stage-dependent part is added
+  // at issue time).  A: one slot covers 1024 / ROWB rows.
+  constexpr int CPR = ROWB / 16;
+  int a_row_off[A_MAX];
+  int a_chunk[A_MAX];
+#pragma unroll
+  for (int i = 0; i < A_MAX; ++i) {
+    const int sl = min(i * NWT + wave, NS_A - 1);
+    const int c16 = sl * 64 + lane;  // 16-byte slot in the stage's A area
+    const int r = c16 / CPR, p = c16 % CPR;
+    a_row_off[i] = min(m0 + r, a.M - 1);
+    a_chunk[i] = swz<ROWB>(r, p);  // chunk whose data belongs at position p of row r
+  }
+  // B: byte o of the stage's weight area is column block o / BSB, byte o % BSB of
+  // it (plus the half-superblock offset of the stage when BSB = 512)
+  int b_off[B_MAX];
+#pragma unroll
+  for (int i = 0; i < B_MAX; ++i) {
+    const int sl = min(i * NWT + wave, NS_B - 1);
+    const int o = (sl * 64 + lane) * 16;
+    b_off[i] = ((n0 >> 4) + o / BSB) * 1024 + o % BSB;
+  }
+
+  auto issue = [&](int st) {  // stage st of this part into ring slot st % NSTAGE
+    const int gs = s0 + min(st, nst - 1);  // clamped: stages past the end are never consumed
+    const int pos = gs * SPOS;
+    const int kb = pos / KB;
+    uint8_t* base = lds + (st % NSTAGE) * STAGE;
+    const size_t apos = (size_t)pos * ESZ;
+#pragma unroll
+    for (int i = 0; i < A_MAX; ++i) {
+      if (NS_A % NWT == 0 || i < la) {
+        const uint8_t* g = Ab + (size_t)a_row_off[i] * a_row_bytes + apos + a_chunk[i] * 16;
+        dma16(g, lds_off(base) + (i * NWT + wave) * 1024);
+      }
+    }
+    const size_t sb_row = (size_t)kb * a.NB * 1024 + (size_t)(pos % KB) * 1024 / KB;
+#pragma unroll
+    for (int i = 0; i < B_MAX; ++i) {
+      if (NS_B % NWT == 0 || i < lb)
+        dma16(Wb + sb_row + b_off[i], lds_off(base) + A_BYTES + (i * NWT + wave) * 1024);
+    }
+    if constexpr (SCALED) {
+      if (wave == 0) {
+        // (scale[, zero]) of columns n0 .. n0 + BN - 1: up to 1 KiB (lanes past the
+        // end re-read the last 16 bytes into the unused part of the slot)
+        const int grp = pos / (a.group_size > 0 ? a.group_size : a.K);
+        constexpr int bytes_per = ZEROS ? 4 : 2;
+        const int off = min(lane * 16, BN * bytes_per - 16);
+        const uint8_t* src = static_cast<const uint8_t*>(a.S) + ((size_t)grp * a.Npad + n0) * bytes_per + off;
+        dma16(src, lds_off(base) + A_BYTES + B_BYTES);
+      }
+    }
+  };
+
+  acc_v acc[WTM][WTN];
+#pragma unroll
+  for (int i = 0; i < WTM; ++i)
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) acc[i][j] = acc_v{0, 0, 0, 0};
+
+  struct Frag {
+    uint4 a[WTM];  // activation fragments (16 rows each)
+    uint4 b[WTN];  // MFMA-ready weight fragments (16 columns each)
+  };
+  // int4 / int2: the packed word a lane feeds to an MFMA step, per column block
+  uint32_t rw[WTN];
+  uint32_t sc[WTN], zc[WTN];
+
+  auto slot = [&](int s) -> const uint8_t* { return lds + (s % NSTAGE) * STAGE; };
+
+  // Round rn (stages rn * KS .. rn * KS + KS - 1, one per K group) becomes
+  // readable: this wave's loads of it are done when at most NSTAGE - 2 KS later
+  // stages of loads are outstanding, and lgkmcnt(0) retires this wave's LDS reads
+  // of the round held in registers, whose ring slots the loads issued after the
+  // barrier overwrite.  A bare s_barrier (a compiler memory barrier through the
+  // clobber) instead of __syncthreads, whose fence would drain the loads still in
+  // flight.
+  auto sync_round = [&](int rn) {
+    wait_loads<G::LMIN, G::LMAX, NSTAGE - 2 * KS>(my_loads);
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < KS; ++k) issue(rn * KS + NSTAGE - KS + k);
+  };
+
+  // keeps the machine scheduler from moving instructions across it, so that the
+  // reads of the next fragments issue before the MFMAs of the current ones and no
+  // MFMA of the next step is hoisted above the barrier that guards its data
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+  // fragments of step t of stage s
+  auto read_step = [&](Frag& f, int s, auto T) {
+    constexpr int t = decltype(T)::value;
+    const uint8_t* base = slot(s);
+    int chunk;
+    if constexpr (PACKED) chunk = (q & 1) * 4 + (2 * t + (q >> 1));  // piece q & 1, word 2t + (q >> 1)
+    else chunk = q;                                                    // 8 fp16 / 16 int8 per lane group
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      const int r = (wm * WTM + i) * 16 + l16;
+      f.a[i] = *reinterpret_cast<const uint4*>(base + r * ROWB + swz<ROWB>(r, chunk) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) {
+      const uint8_t* lb = base + A_BYTES + (wn * WTN + j) * BSB;
+      if constexpr (PACKED)
+        rw[j] = *reinterpret_cast<const uint32_t*>(lb + ((q & 1) * 16 + l16) * 16 + (2 * t + (q >> 1)) * 4);
+      else
+        f.b[j] = *reinterpret_cast<const uint4*>(lb + lane * 16);  // whole superblock, piece = lane
+      if constexpr (SCALED && t == 0) {
+        const int col = (wn * WTN + j) * 16 + l16;
+        if constexpr (ZEROS) {
+          const uint32_t u = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4);
+          sc[j] = (u & 0xFFFFu) * 0x10001u;
+          zc[j] = (u >> 16) * 0x10001u;
+        } else {
+          const uint32_t u = *reinterpret_cast<const uint16_t*>(base + A_BYTES + B_BYTES + col * 2);
+          sc[j] = u * 0x10001u;
+          zc[j] = 0;
+        }
+      }
+    }
+  };
+
+  // upcast of column block j from its packed word (int4 / int2 only)
+  auto make_b = [&](Frag& f, int j) {
+    if constexpr (PACKED) {
+      const uint32_t wd = rw[j];
+      uint32_t o[4];
+      if constexpr (I4) {
+        constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          half2v v = as_h2(and_or(wd >> (4 * jj), 0x000F000Fu, 0x64006400u)) - as_h2(bias);
+          if constexpr (ZEROS) v = v - as_h2(zc[j]);
+          if constexpr (SCALED) v = v * as_h2(sc[j]);
+          o[jj] = as_u32(v);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 3; ++jj)  // offset-binary classes: 0,1,2,3 -> -2,-1,0,1
+          o[jj] = __builtin_amdgcn_perm(0u, 0x0100FFFEu, (wd >> (2 * jj)) & 0x03030303u);
+        // two's complement class: 0,1,2,3 -> 0,1,-2,-1
+        o[3] = __builtin_amdgcn_perm(0u, 0xFFFE0100u, (wd >> 6) & 0x03030303u);
+      }
+      f.b[j] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
+  auto mma = [&](const Frag& f, int j) {
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      if constexpr (FP)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(half8v, f.a[i]), __builtin_bit_cast(half8v, f.b[j]), acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            __builtin_bit_cast(int4v, f.a[i]), __builtin_bit_cast(int4v, f.b[j]), acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // one MFMA step on cur while nxt (already read) is upcast, block by block
+  auto compute = [&](const Frag& cur, Frag& nxt) {
+    fence();
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) {
+      mma(cur, j);
+      make_b(nxt, j);
+    }
+    fence();
+  };
+
+  // prologue: NSTAGE stages in flight, then the fragments of step 0
+#pragma unroll
+  for (int st = 0; st < NSTAGE; ++st) issue(st);
+  wait_loads<G::LMIN, G::LMAX, NSTAGE - KS>(my_loads);
+  asm volatile("s_barrier" ::: "memory");
+
+  Frag X, Y;
+  read_step(X, kg, std::integral_constant<int, 0>{});
+#pragma unroll
+  for (int j = 0; j < WTN; ++j) make_b(X, j);
+
+  if constexpr (NSTEP == 1) {
+    // one MFMA step per stage, two stages per iteration
+    int s = 0;
+    for (; s + 1 < nst; s += 2) {
+      sync_round(s + 1);
+      fence();
+      read_step(Y, s + 1, std::integral_constant<int, 0>{});
+      compute(X, Y);
+      sync_round(s + 2);  // past the last stage this reads clamped copies that are never used
+      fence();
+      read_step(X, s + 2, std::integral_constant<int, 0>{});
+      compute(Y, X);
+    }
+    if (s < nst) compute(X, Y);
+  } else {
+    // two MFMA steps per stage: X holds step 0 of this group's stage of round r,
+    // Y step 1.  In a last, partial round the groups past the end only keep the
+    // barriers (their reads hit clamped copies and are not used).
+    const int nr = (nst + KS - 1) / KS;
+    for (int r = 0; r < nr; ++r) {
+      const int s = r * KS + kg;
+      const bool live = KS == 1 || s < nst;
+      fence();
+      read_step(Y, s, std::integral_constant<int, 1>{});
+      if (live) compute(X, Y);
+      sync_round(r + 1);  // past the last round this reads clamped copies that are never used
+      fence();
+      read_step(X, s + KS, std::integral_constant<int, 0>{});
+      if (live) compute(Y, X);
+    }
+  }
+  wait_vmcnt<0>();  // drain the clamped tail loads before the workgroup's LDS is released
+
+  if constexpr (KS > 1) {
+    // K groups 1.. hand their partial sums to group 0 through the (now idle)
+    // ring, which adds them in group order
+    __syncthreads();
+    acc_v* red = reinterpret_cast<acc_v*>(lds);
+    if (kg > 0) {
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j) red[(kg - 1) * G::RED + ((wl * WTM + i) * WTN + j) * 64 + lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (kg != 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; ++g)
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j) acc[i][j] += red[(g - 1) * G::RED + ((wl * WTM + i) * WTN + j) * 64 + lane];
+  }
+
+  // epilogue: lane l holds rows 4 (l / 16) + r, column l % 16 of each 16 x 16 sub-tile
+#pragma unroll
+  for (int i = 0; i < WTM; ++i)
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) {
+      const int col = n0 + (wn * WTN + j) * 16 + l16;
+      if (col >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + (wm * WTM + i) * 16 + q * 4 + r;
+        if (row >= a.M) continue;
+        const size_t o = (size_t)row * a.N + col;
+        const auto v = acc[i][j][r];
+        if (a.out_mode == OUT_STORE) {
+          if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)v;
+          else static_cast<int*>(a.C)[o] = v;
+        } else if (a.out_mode == OUT_ATOMIC) {
+          if constexpr (FP) unsafeAtomicAdd(static_cast<float*>(a.ws) + o, v);
+          else atomicAdd(static_cast<int*>(a.C) + o, v);
+        } else {
+          if constexpr (FP) static_cast<float*>(a.ws)[(size_t)part * a.M * a.N + o] = v;
+          else static_cast<int*>(a.ws)[(size_t)part * a.M * a.N + o] = v;
+        }
+      }
+    }
+}
+
+// the tile configurations: rows x columns; waves rows x columns x K groups.  Up
+// to 128 rows the waves never split the rows, so every weight fragment is
+// upcast once per workgroup; int4 / int2 (P) take K groups on the smaller tiles,
+// fp16 / int8 (F) split the columns only.
+#ifndef QG_DL_WAVES_P_32x64
+#define QG_DL_WAVES_P_32x64 1, 2, 4
+#endif
+#ifndef QG_DL_WAVES_F_32x64
+#define QG_DL_WAVES_F_32x64 1, 4, 1
+#endif
+#ifndef QG_DL_WAVES_P_32x128
+#define QG_DL_WAVES_P_32x128 1, 2, 4
+#endif
+#ifndef QG_DL_WAVES_F_32x128
+#define QG_DL_WAVES_F_32x128 1, 4, 1
+#endif
+#ifndef QG_DL_WAVES_P_32x256
+#define QG_DL_WAVES_P_32x256 1, 4, 2
+#endif
+#ifndef QG_DL_WAVES_F_32x256
+#define QG_DL_WAVES_F_32x256 1, 8, 1
+#endif
+#ifndef QG_DL_WAVES_P_64x128
+#define QG_DL_WAVES_P_64x128 1, 2, 2
+#endif
+#ifndef QG_DL_WAVES_F_64x128
+#define QG_DL_WAVES_F_64x128 1, 4, 1
+#endif
+#ifndef QG_DL_WAVES_P_64x256
+#define QG_DL_WAVES_P_64x256 1, 4, 2
+#endif
+#ifndef QG_DL_WAVES_F_64x256
+#define QG_DL_WAVES_F_64x256 1, 8, 1
+#endif
+#ifndef QG_DL_WAVES_P_128x256
+#define QG_DL_WAVES_P_128x256 1, 8, 1
+#endif
+#ifndef QG_DL_WAVES_F_128x256
+#define QG_DL_WAVES_F_128x256 1, 8, 1
+#endif
+#ifndef QG_DL_WAVES_P_256x256
+#define QG_DL_WAVES_P_256x256 2, 4, 1
+#endif
+#ifndef QG_DL_WAVES_F_256x256
+#define QG_DL_WAVES_F_256x256 2, 4, 1
+#endif
+template <int FMT, bool SCALED, int T> struct TileGeo;
+template <int FMT, int BM, int BN, bool SCALED, int PWM, int PWN, int PKS, int FWM, int FWN, int FKS>
+using GeoOf = typename std::conditional<(FMT == FMT_I4 || FMT == FMT_U4 || FMT == FMT_I2),
+                                        Geo<FMT, BM, BN, PWM, PWN, PKS, SCALED>,
+                                        Geo<FMT, BM, BN, FWM, FWN, FKS, SCALED>>::type;
+#define QG_DL_TILE(T, BM, BN, SHAPE)                                                            \
+  template <int FMT, bool SCALED> struct TileGeo<FMT, SCALED, T> {                              \
+    using type = GeoOf<FMT, BM, BN, SCALED, QG_DL_WAVES_P_##SHAPE, QG_DL_WAVES_F_##SHAPE>;      \
+  };
+QG_DL_TILE(DL_32x64, 32, 64, 32x64)
+QG_DL_TILE(DL_32x128, 32, 128, 32x128)
+QG_DL_TILE(DL_32x256, 32, 256, 32x256)
+QG_DL_TILE(DL_64x128, 64, 128, 64x128)
+QG_DL_TILE(DL_64x256, 64, 256, 64x256)
+QG_DL_TILE(DL_128x256, 128, 256, 128x256)
+QG_DL_TILE(DL_256x256, 256, 256, 256x256)
+#undef QG_DL_TILE
+
+template <int FMT, int T, bool SCALED, bool ZEROS>
+hipError_t launch_t(const RunArgs& a, hipStream_t st) {
+  using G = typename TileGeo<FMT, SCALED, T>::type;
+  static_assert((size_t)G::STAGE * G::NSTAGE <= 160 * 1024, "LDS budget");
+  const int tiles = ((a.M + G::BM - 1) / G::BM) * ((a.N + G::BN - 1) / G::BN);
+  hipLaunchKernelGGL((mfma_dl_kernel<FMT, G, SCALED, ZEROS>), dim3(tiles * a.k_parts), dim3(G::NWT * 64), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+template <int T>
+hipError_t launch_tile(int fmt, const RunArgs& a, hipStream_t st) {
+  const bool sc = a.smode != SC_NONE;
+  switch (fmt) {
+    case FMT_F16: return launch_t<FMT_F16, T, false, false>(a, st);
+    case FMT_I8: return launch_t<FMT_I8, T, false, false>(a, st);
+    case FMT_I2: return launch_t<FMT_I2, T, false, false>(a, st);
+    case FMT_I4: return sc ? launch_t<FMT_I4, T, true, false>(a, st) : launch_t<FMT_I4, T, false, false>(a, st);
+    case FMT_U4:
+      return !sc ? launch_t<FMT_U4, T, false, false>(a, st)
+           : a.zeros ? launch_t<FMT_U4, T, true, true>(a, st) : launch_t<FMT_U4, T, true, false>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+void dl_tile_dims(int tile, int* bm, int* bn) {
+  static const int dims[DL_NUM][2] = {{32, 64}, {32, 128}, {32, 256}, {64, 128}, {64, 256}, {128, 256}, {256, 256}};
+  *bm = dims[tile][0];
+  *bn = dims[tile][1];
+}
+
+int choose_dl_tile(int fmt, int64_t M, int64_t N, int k_parts, int smode) {
+  const bool packed = fmt == FMT_I4 || fmt == FMT_U4 || fmt == FMT_I2;
+  if (packed && smode == SC_PIECE) return -1;  // one scale slot per stage holds one group per column
+  const int cap = M <= 32 ? 32 : M <= 64 ? 64 : M <= 128 ? 128 : 256;
+  static const int order[] = {DL_256x256, DL_128x256, DL_64x256, DL_64x128, DL_32x256, DL_32x128, DL_32x64};
+#ifdef QG_FORCE_DL_TILE
+  if (QG_FORCE_DL_TILE >= 0) return QG_FORCE_DL_TILE;
+#endif
+  // The largest tile whose last wave of workgroups still occupies at least 60% of
+  // the 256 CUs: larger tiles re-read less of A and B, idle CUs cost in proportion.
+  int pick = -1;
+  for (int t : order) {
+    int bm, bn;
+    dl_tile_dims(t, &bm, &bn);
+    if (bm > cap) continue;
+    pick = t;
+    const int64_t wgs = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * k_parts;
+    const int64_t waves = (wgs + 255) / 256;
+    if (wgs * 10 >= waves * 256 * 6) break;
+  }
+  return pick;
+}
+
+hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st) {
+  switch (tile) {
+    case DL_32x64: return launch_tile<DL_32x64>(fmt, a, st);
+    case DL_32x128: return launch_tile<DL_32x128>(fmt, a, st);
+    case DL_32x256: return launch_tile<DL_32x256>(fmt, a, st);
+    case DL_64x128: return launch_tile<DL_64x128>(fmt, a, st);
+    case DL_64x256: return launch_tile<DL_64x256>(fmt, a, st);
+    case DL_128x256: return launch_tile<DL_128x256>(fmt, a, st);
+    case DL_256x256: return launch_tile<DL_256x256>(fmt, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qg

@@ -87,9 +87,12 @@ hipError_t launch_pack(const Layout& L, const void* w, const void* s, const void
                        hipStream_t st);
 hipError_t launch_gemv(int fmt, const RunArgs& a, hipStream_t st);
 hipError_t launch_mfma(int fmt, int tile, const RunArgs& a, hipStream_t st);
-// 256 x 256 tiles with a direct-load LDS ring (M large); not for per-piece scale groups
-bool big_tile_supported(int fmt, const RunArgs& a);
-hipError_t launch_mfma_big(int fmt, const RunArgs& a, hipStream_t st);
+// direct-load ring kernel (mfma_dl.hip): the tile for a problem, or -1 when the
+// problem needs the LDS-staged kernel (int4 with per-piece scale groups)
+enum DlTile : int { DL_32x64 = 0, DL_32x128, DL_32x256, DL_64x128, DL_64x256, DL_128x256, DL_256x256, DL_NUM };
+void dl_tile_dims(int tile, int* bm, int* bn);
+int choose_dl_tile(int fmt, int64_t M, int64_t N, int k_parts, int smode);
+hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st);
 
@@ -103,9 +106,8 @@ hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st);
 #endif
 constexpr int GEMV_MAX_WAVES = QG_GEMV_MAX_WAVES;
 
-// MFMA tile configurations (BM x BN, waves WM x WN)
-// TILE_BIG is 256 x 256 (the direct-load ring kernel; the LDS-staged kernel serves it as
-// 256 x 256 for fp16 / int8 and 256 x 128 for int4 / int2 when per-piece scale groups are used)
+// tiles of the LDS-staged MFMA kernel (mfma.hip), used where the direct-load kernel
+// is not: TILE_BIG is 256 x 256 for fp16 / int8 and 256 x 128 for int4 / int2
 enum Tile : int { TILE_32x64 = 0, TILE_64x64 = 1, TILE_128x128 = 2, TILE_BIG = 3 };
 void tile_dims(int fmt, int tile, int* bm, int* bn);
 
