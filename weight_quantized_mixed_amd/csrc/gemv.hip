@@ -104,8 +104,10 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
   // rows kb0 + w, kb0 + w + waves, ...), so at any moment the whole grid streams
   // one narrow band of consecutive 1 KiB superblock rows, which the memory system
   // serves much faster than one contiguous run per wave spread over the matrix.
-  const int cnt = kb1 - kb0 > wave ? (kb1 - kb0 - wave + a.waves - 1) / a.waves : 0;  // rows of this wave
-  auto row_of = [&](int j) { return kb0 + wave + j * a.waves; };
+  // (wave-uniform: readfirstlane keeps the loop counter and row index in scalar
+  // registers, which the compiler does not infer by itself here)
+  const int cnt = __builtin_amdgcn_readfirstlane(kb1 - kb0 > wave ? (kb1 - kb0 - wave + a.waves - 1) / a.waves : 0);
+  auto row_of = [&](int j) { return __builtin_amdgcn_readfirstlane(kb0 + wave + j * a.waves); };
 
   cptr A = (cptr)a.A;
   const uint32_t* __restrict__ Av = static_cast<const uint32_t*>(a.A);
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
 #pragma unroll
   for (int m = 0; m < MR; ++m) tot[m] = 0;
 
-  constexpr int UNR = QG_GEMV_UNR;
+  constexpr int UNR = FMT == FMT_I2 ? QG_GEMV_UNR_I2 : QG_GEMV_UNR;
   struct Stage {
     uint4 w[UNR][4];
     uint32_t as[UNR][MR];

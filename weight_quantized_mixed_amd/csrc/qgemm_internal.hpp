@@ -104,6 +104,9 @@ hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st);
 #ifndef QG_GEMV_UNR
 #define QG_GEMV_UNR 1
 #endif
+#ifndef QG_GEMV_UNR_I2
+#define QG_GEMV_UNR_I2 1
+#endif
 constexpr int GEMV_MAX_WAVES = QG_GEMV_MAX_WAVES;
 
 // tiles of the LDS-staged MFMA kernel (mfma.hip), used where the direct-load kernel
