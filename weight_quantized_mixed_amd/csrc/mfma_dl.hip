@@ -31,7 +31,7 @@
 // is upcast twice.
 //
 // Workgroups are numbered so each XCD owns a contiguous band of tiles, swept in
-// column-major groups of 8 tile rows (L2 reuse of the shared A / B blocks, the
+// column-major groups of a few tile rows (L2 reuse of the shared A / B blocks, the
 // traversal point of the mKernel AG-GEMM PR #41 discussion).
 #include <type_traits>
 #include <utility>
@@ -109,6 +109,12 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, T...>, F&&
   (f(std::integral_constant<int, T>{}), ...);
 }
 
+#ifndef QG_DL_GROUP_M
+#define QG_DL_GROUP_M 8
+#endif
+#ifndef QG_DL_GROUP_M_BIG
+#define QG_DL_GROUP_M_BIG 2
+#endif
 #ifndef QG_DL_MAXST
 #define QG_DL_MAXST 16
 #endif
@@ -188,7 +194,9 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   const int part = w / tiles;
   w -= part * tiles;
   if ((tiles & 7) == 0) w = (w & 7) * (tiles >> 3) + (w >> 3);
-  constexpr int GROUP_M = 8;
+  // column-major groups of tile rows: 2 for the 256-row tiles (their A row blocks
+  // then stay in the last-level cache between column sweeps), 8 otherwise
+  constexpr int GROUP_M = BM == 256 ? QG_DL_GROUP_M_BIG : QG_DL_GROUP_M;
   const int group = w / (GROUP_M * tiles_n);
   const int first_m = group * GROUP_M;
   const int gsz = min(tiles_m - first_m, GROUP_M);
