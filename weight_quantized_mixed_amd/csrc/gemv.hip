@@ -129,9 +129,9 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
     uint32_t sc[UNR];  // raw scale (or scale | zero << 16) of the superblock's group
   };
 
-  // Every stage issues the same loads (superblocks past the wave's range re-read
-  // its last one and are not used), so the compiler can count outstanding loads
-  // exactly and never has to drain the next stage to use this one.
+  // Every stage issues the same loads (in a partial stage, superblocks past the
+  // wave's range re-read its last one and are not used), so the compiler can count
+  // outstanding loads exactly and never has to drain the next stage to use this one.
   auto load = [&](Stage& s, int j) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -461,22 +461,49 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
     else do_block_rows(wv, as, sc, kb);
   };
 
-  // two register stages: loads of the next UNR superblocks fly while these are consumed
+  // Two register stages: the loads of the next UNR superblocks fly while these are
+  // consumed.
   Stage s0, s1;
-  int j = 0;
-  if (j < cnt) load(s0, j);
-  while (j < cnt) {
-    load(s1, j + UNR);
+  auto consume = [&](const Stage& s, int j) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
-      if (j + u < cnt) block(s0.w[u], s0.as[u], s0.sc[u], row_of(j + u));
-    j += UNR;
-    if (j >= cnt) break;
-    load(s0, j + UNR);
-#pragma unroll
-    for (int u = 0; u < UNR; ++u)
-      if (j + u < cnt) block(s1.w[u], s1.as[u], s1.sc[u], row_of(j + u));
-    j += UNR;
+      if (j + u < cnt) block(s.w[u], s.as[u], s.sc[u], row_of(j + u));
+  };
+  if constexpr (MR == 1 && !I4) {
+    // The steady loop runs while two more stages remain, so it never loads past
+    // the wave's rows; the last one or two stages follow it (faster for the
+    // small int8 / int2 / fp16 blocks, whose code can be repeated).
+    if (cnt > 0) {
+      int j = 0;
+      load(s0, 0);
+      for (; j + 2 * UNR < cnt; j += 2 * UNR) {
+        load(s1, j + UNR);
+        consume(s0, j);
+        load(s0, j + 2 * UNR);
+        consume(s1, j + UNR);
+      }
+      if (j + UNR < cnt) {
+        load(s1, j + UNR);
+        consume(s0, j);
+        consume(s1, j + UNR);
+      } else {
+        consume(s0, j);
+      }
+    }
+  } else {
+    // one copy of each stage's block code: the last stage loads a clamped copy
+    // of the wave's last superblock that is never used
+    int j = 0;
+    if (j < cnt) load(s0, j);
+    while (j < cnt) {
+      load(s1, j + UNR);
+      consume(s0, j);
+      j += UNR;
+      if (j >= cnt) break;
+      load(s0, j + UNR);
+      consume(s1, j);
+      j += UNR;
+    }
   }
 
   // block reduction across the waves of the workgroup
