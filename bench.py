@@ -44,8 +44,8 @@ def alg_bytes(M, N, K, w_dtype, g, zeros):
 
 def label(c):
     s = f"{c['w']} M={c['M']} N={c['N']} K={c['K']}"
-    if c.get("g"):
-        s += f" g={c['g']}"
+    if c["w"] in ("i4", "u4"):
+        s += f" g={c.get('g', 0)}"
     if c.get("zeros"):
         s += " zeros"
     if c.get("kp", 1) > 1:
@@ -124,7 +124,7 @@ class Bench:
         self.q.close()
 
 
-def measure_grid_entry(b, bursts=15):
+def measure_grid_entry(b, bursts=50):
     import statistics
     b.timed(5)
     per = max(len(b.packed), 8)
@@ -149,6 +149,7 @@ GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128
         + [{"w": "i4", "M": M, "N": N, "K": K, "g": 128, "kp": kp} for M in (1, 128)
            for (K, N) in ((4096, 11008), (11008, 4096), (4096, 4096), (4096, 32000)) for kp in (1, 4)]
         + [{"w": "i4", "M": 1, "N": 4096, "K": 4096, "g": 128}]
+        + [{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": g} for g in (0, -1) for M in (1, 32, 128, 512)]
         + [{"w": "f16", "M": 16384, "N": 16384, "K": 16384},
            {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}])
 
