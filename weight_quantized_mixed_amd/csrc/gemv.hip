@@ -464,6 +464,12 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
   // Two register stages: the loads of the next UNR superblocks fly while these are
   // consumed.
   Stage s0, s1;
+  // keeps the machine scheduler from sinking a stage's loads below the block
+  // code that follows them, which it does for the unscaled int4 variant (draining
+  // the prefetch); the other variants are scheduled better without it
+  auto fence = [] {
+    if constexpr (I4 && VAR == 0) __builtin_amdgcn_sched_barrier(0);
+  };
   auto consume = [&](const Stage& s, int j) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
@@ -478,12 +484,15 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
       load(s0, 0);
       for (; j + 2 * UNR < cnt; j += 2 * UNR) {
         load(s1, j + UNR);
+        fence();
         consume(s0, j);
         load(s0, j + 2 * UNR);
+        fence();
         consume(s1, j + UNR);
       }
       if (j + UNR < cnt) {
         load(s1, j + UNR);
+        fence();
         consume(s0, j);
         consume(s1, j + UNR);
       } else {
@@ -497,10 +506,12 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
     if (j < cnt) load(s0, j);
     while (j < cnt) {
       load(s1, j + UNR);
+      fence();
       consume(s0, j);
       j += UNR;
       if (j >= cnt) break;
       load(s0, j + UNR);
+      fence();
       consume(s1, j);
       j += UNR;
     }
