@@ -36,6 +36,12 @@ SMALL = [
     (8, 136, 512, "i8", 0, False),
     (1, 200, 2048, "i2", 0, False),
     (5, 72, 1024, "i2", 0, False),
+    (1, 88, 512, "i4", 64, False),
+    (1, 136, 1024, "i4", 0, False),
+    # M = 1 with 16-column workgroups at k_parts 1, 64-column blocks at k_parts 3
+    (1, 2752, 512, "u4", 128, True),
+    (1, 2752, 1024, "i2", 0, False),
+    (1, 2752, 256, "f16", 0, False),
     # MFMA path (M > 8): several tiles and ragged tails in M and N
     (9, 72, 512, "i4", 128, False),
     (33, 200, 1024, "i4", 128, False),
@@ -193,3 +199,40 @@ def test_direct_load_tiles(M, N, kp, det, w_dtype, g, zeros):
     cols = np.unique(np.concatenate([rng.choice(N, 400, replace=False), [0, 63, 64, 255, 256, N - 1]]))
     gpu = c.run()
     assert_matches(gpu[:, cols], c.reference(cols=cols), f"dl {w_dtype} M={M} kp={kp}")
+
+
+# ---------------------------------------------------------------- HIP graph capture
+GRAPH_CASES = [(1, 200, 1024, "i4", 128, False, 1, False), (1, 2752, 1024, "i2", 0, False, 3, False),
+               (4, 300, 1024, "u4", 128, True, 1, False), (40, 264, 1024, "i4", 128, False, 2, False),
+               (40, 264, 1024, "i8", 0, False, 2, True), (300, 520, 512, "f16", 0, False, 1, False)]
+
+
+@pytest.mark.parametrize("M,N,K,w_dtype,g,zeros,kp,det", GRAPH_CASES)
+def test_graph_replays_match_eager(M, N, K, w_dtype, g, zeros, kp, det):
+    """qgemm_run captured in a HIP graph (with its zero-fill and finalize kernels for
+    split-K): every replay, with eager work between them, gives the eager result."""
+    say(f"graph M={M} N={N} K={K} {w_dtype} g={g} zeros={zeros} kp={kp} det={det}")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=11 * M + N)
+    eager = c.run()
+    C = c.q.new_output()
+    ws = c.q.workspace()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            c.q.run(c.A, c.packed, C, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    exact = w_dtype in ("i8", "i2") or kp == 1 or det
+    for r in range(3):
+        C.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        if exact:
+            assert np.array_equal(got, eager), f"replay {r} differs from the eager result"
+        else:  # fp32 atomics: summation order may differ between runs
+            assert_matches(got.astype(np.float64), eager.astype(np.float64), f"graph replay {r}")
+        c.run()  # eager work between replays
+        torch.cuda.synchronize()

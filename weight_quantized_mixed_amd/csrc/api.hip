@@ -20,6 +20,7 @@ struct qgemm_plan {
   int dl_tile;       // direct-load MFMA tile, or -1
   int tile;          // LDS-staged MFMA tile (used when dl_tile < 0)
   int gemv_waves;    // GEMV waves per workgroup
+  bool gemv_narrow;  // M = 1 with fewer than 128 blocks of 64 columns: 16-column workgroups
   int32_t unit_kb, n_units;
   size_t ws_bytes;
 };
@@ -62,8 +63,17 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
 #define QG_GEMV_TARGET_WAVES 2048
 #endif
 
+// M = 1 and so few 64-column blocks that they would occupy under half of the 256
+// CUs (with more, the 64-column kernel is faster: measured at N = 4096 .. 32000)
+#ifndef QG_GEMV_NARROW_BELOW
+#define QG_GEMV_NARROW_BELOW 128
+#endif
+bool choose_gemv_narrow(const qgemm_plan* p) {
+  return p->path == QGEMM_PATH_GEMV && p->M == 1 && (p->N + 63) / 64 * p->k_parts < QG_GEMV_NARROW_BELOW;
+}
+
 int choose_gemv_waves(const qgemm_plan* p) {
-  const int64_t rb = (p->N + 63) / 64;
+  const int64_t rb = (p->N + (p->gemv_narrow ? 15 : 63)) / (p->gemv_narrow ? 16 : 64);
   const int64_t per_part = p->L.nkb / p->k_parts;
   int64_t want = (QG_GEMV_TARGET_WAVES + rb * p->k_parts - 1) / (rb * p->k_parts);
   int64_t maxw = per_part / 2;
@@ -176,6 +186,7 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
                    ? choose_dl_tile(fmt, M, N, k_parts,
                                     group_size == 0 ? SC_NONE : (group_size > 0 && group_size < KB) ? SC_PIECE : SC_BLOCK)
                    : -1;
+  p->gemv_narrow = choose_gemv_narrow(p);
   p->gemv_waves = choose_gemv_waves(p);
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   if (k_parts == 1) p->ws_bytes = 0;
@@ -213,7 +224,8 @@ qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed
   if (a.out_mode == OUT_ATOMIC)
     e = launch_fill_zero(out_f16 ? workspace : C, (size_t)plan->M * plan->N * 4, st);
   if (e == hipSuccess)
-    e = plan->path == QGEMM_PATH_GEMV ? launch_gemv(plan->L.fmt, a, st)
+    e = plan->path == QGEMM_PATH_GEMV ? (plan->gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
+                                                           : launch_gemv(plan->L.fmt, a, st))
         : plan->dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, plan->dl_tile, a, st)
         : launch_mfma(plan->L.fmt, plan->tile, a, st);
   if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))
