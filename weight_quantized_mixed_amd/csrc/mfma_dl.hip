@@ -118,6 +118,17 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, T...>, F&&
 #ifndef QG_DL_MAXST
 #define QG_DL_MAXST 16
 #endif
+#ifndef QG_DL_IL
+#define QG_DL_IL 1
+#endif
+// int4 / int2 stages: 0 keeps the upcasts in a run after each step's MFMAs,
+// 1 spreads them word by word, 2 column block by column block (per tile height)
+#ifndef QG_DL_IL_P
+#define QG_DL_IL_P 2
+#endif
+#ifndef QG_DL_IL_P_BIG
+#define QG_DL_IL_P_BIG 0
+#endif
 
 // Stage geometry of a tile configuration.
 template <int FMT, int BM_, int BN_, int WM_, int WN_, int KS_, bool SCALED>
@@ -161,10 +172,14 @@ struct Geo {
 // s_waitcnt vmcnt(MUL * n) lgkmcnt(0) for a wave-uniform n in [LO, HI]
 template <int LO, int HI, int MUL>
 __device__ __forceinline__ void wait_loads(int n) {
-  static_for(std::make_integer_sequence<int, HI - LO + 1>{}, [&](auto T) {
-    constexpr int v = LO + decltype(T)::value;
-    if (n == v) wait_vm_lgkm0<MUL * v>();
-  });
+  if constexpr (LO == HI) {
+    wait_vm_lgkm0<MUL * LO>();  // every wave issues the same count
+  } else {
+    static_for(std::make_integer_sequence<int, HI - LO + 1>{}, [&](auto T) {
+      constexpr int v = LO + decltype(T)::value;
+      if (n == v) wait_vm_lgkm0<MUL * v>();
+    });
+  }
 }
 
 template <int FMT, class G, bool SCALED, bool ZEROS>
@@ -176,6 +191,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   constexpr int SPOS = G::SPOS, ROWB = G::ROWB, BSB = G::BSB, NSTAGE = G::NSTAGE, NSTEP = G::NSTEP;
   constexpr int KB = G::KB, ESZ = G::ESZ;
   constexpr int A_BYTES = G::A_BYTES, B_BYTES = G::B_BYTES, STAGE = G::STAGE;
+  constexpr int ILP = BM == 256 ? QG_DL_IL_P_BIG : QG_DL_IL_P;  // measured per tile height
   constexpr int NS_A = G::NS_A, NS_B = G::NS_B, A_MAX = G::A_MAX, B_MAX = G::B_MAX;
   typedef typename std::conditional<FP, float4v, int4v>::type acc_v;
 
@@ -242,36 +258,45 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
     b_off[i] = ((n0 >> 4) + o / BSB) * 1024 + o % BSB;
   }
 
-  auto issue = [&](int st) {  // stage st of this part into ring slot st % NSTAGE
+  // where stage st of this part goes (ring slot st % NSTAGE) and comes from
+  struct StageSrc {
+    uint32_t dst;   // LDS byte address of the slot
+    size_t apos;    // byte offset of the stage in an activation row
+    size_t sb_row;  // byte offset of the stage's weights in the blob (column block 0)
+    int grp;        // scale group
+  };
+  auto stage_src = [&](int st) {
+    StageSrc r;
     const int gs = s0 + min(st, nst - 1);  // clamped: stages past the end are never consumed
     const int pos = gs * SPOS;
-    const int kb = pos / KB;
-    uint8_t* base = lds + (st % NSTAGE) * STAGE;
-    const size_t apos = (size_t)pos * ESZ;
-#pragma unroll
-    for (int i = 0; i < A_MAX; ++i) {
-      if (NS_A % NWT == 0 || i < la) {
-        const uint8_t* g = Ab + (size_t)a_row_off[i] * a_row_bytes + apos + a_chunk[i] * 16;
-        dma16(g, lds_off(base) + (i * NWT + wave) * 1024);
-      }
+    r.dst = lds_off(lds + (st % NSTAGE) * STAGE);
+    r.apos = (size_t)pos * ESZ;
+    r.sb_row = (size_t)(pos / KB) * a.NB * 1024 + (size_t)(pos % KB) * 1024 / KB;
+    r.grp = SCALED ? pos / (a.group_size > 0 ? a.group_size : a.K) : 0;
+    return r;
+  };
+  // this wave's direct load e of a stage: A slots, then B slots, then (wave 0) scales
+  constexpr int NDMA = A_MAX + B_MAX + (SCALED ? 1 : 0);
+  auto dma_one = [&](const StageSrc& sa, auto E) {
+    constexpr int e = decltype(E)::value;
+    if constexpr (e < A_MAX) {
+      if (NS_A % NWT == 0 || e < la)
+        dma16(Ab + (size_t)a_row_off[e] * a_row_bytes + sa.apos + a_chunk[e] * 16, sa.dst + (e * NWT + wave) * 1024);
+    } else if constexpr (e < A_MAX + B_MAX) {
+      constexpr int i = e - A_MAX;
+      if (NS_B % NWT == 0 || i < lb) dma16(Wb + sa.sb_row + b_off[i], sa.dst + A_BYTES + (i * NWT + wave) * 1024);
+    } else if (wave == 0) {
+      // (scale[, zero]) of columns n0 .. n0 + BN - 1: up to 1 KiB (lanes past the
+      // end re-read the last 16 bytes into the unused part of the slot)
+      constexpr int bytes_per = ZEROS ? 4 : 2;
+      const int off = min(lane * 16, BN * bytes_per - 16);
+      const uint8_t* src = static_cast<const uint8_t*>(a.S) + ((size_t)sa.grp * a.Npad + n0) * bytes_per + off;
+      dma16(src, sa.dst + A_BYTES + B_BYTES);
     }
-    const size_t sb_row = (size_t)kb * a.NB * 1024 + (size_t)(pos % KB) * 1024 / KB;
-#pragma unroll
-    for (int i = 0; i < B_MAX; ++i) {
-      if (NS_B % NWT == 0 || i < lb)
-        dma16(Wb + sb_row + b_off[i], lds_off(base) + A_BYTES + (i * NWT + wave) * 1024);
-    }
-    if constexpr (SCALED) {
-      if (wave == 0) {
-        // (scale[, zero]) of columns n0 .. n0 + BN - 1: up to 1 KiB (lanes past the
-        // end re-read the last 16 bytes into the unused part of the slot)
-        const int grp = pos / (a.group_size > 0 ? a.group_size : a.K);
-        constexpr int bytes_per = ZEROS ? 4 : 2;
-        const int off = min(lane * 16, BN * bytes_per - 16);
-        const uint8_t* src = static_cast<const uint8_t*>(a.S) + ((size_t)grp * a.Npad + n0) * bytes_per + off;
-        dma16(src, lds_off(base) + A_BYTES + B_BYTES);
-      }
-    }
+  };
+  auto issue = [&](int st) {
+    const StageSrc sa = stage_src(st);
+    static_for(std::make_integer_sequence<int, NDMA>{}, [&](auto E) { dma_one(sa, E); });
   };
 
   acc_v acc[WTM][WTN];
@@ -309,63 +334,74 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   // MFMA of the next step is hoisted above the barrier that guards its data
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
-  // fragments of step t of stage s
-  auto read_step = [&](Frag& f, int s, auto T) {
-    constexpr int t = decltype(T)::value;
-    const uint8_t* base = slot(s);
+  // fragment pieces of step t of the stage in the slot at base: activation rows
+  // i (16 each), then the weights of column block j (with the stage's scales
+  // when t = 0)
+  auto read_a = [&](Frag& f, const uint8_t* base, auto T, auto I) {
+    constexpr int t = decltype(T)::value, i = decltype(I)::value;
     int chunk;
     if constexpr (PACKED) chunk = (q & 1) * 4 + (2 * t + (q >> 1));  // piece q & 1, word 2t + (q >> 1)
     else chunk = q;                                                    // 8 fp16 / 16 int8 per lane group
-#pragma unroll
-    for (int i = 0; i < WTM; ++i) {
-      const int r = (wm * WTM + i) * 16 + l16;
-      f.a[i] = *reinterpret_cast<const uint4*>(base + r * ROWB + swz<ROWB>(r, chunk) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < WTN; ++j) {
-      const uint8_t* lb = base + A_BYTES + (wn * WTN + j) * BSB;
-      if constexpr (PACKED)
-        rw[j] = *reinterpret_cast<const uint32_t*>(lb + ((q & 1) * 16 + l16) * 16 + (2 * t + (q >> 1)) * 4);
-      else
-        f.b[j] = *reinterpret_cast<const uint4*>(lb + lane * 16);  // whole superblock, piece = lane
-      if constexpr (SCALED && t == 0) {
-        const int col = (wn * WTN + j) * 16 + l16;
-        if constexpr (ZEROS) {
-          const uint32_t u = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4);
-          sc[j] = (u & 0xFFFFu) * 0x10001u;
-          zc[j] = (u >> 16) * 0x10001u;
-        } else {
-          const uint32_t u = *reinterpret_cast<const uint16_t*>(base + A_BYTES + B_BYTES + col * 2);
-          sc[j] = u * 0x10001u;
-          zc[j] = 0;
-        }
+    const int r = (wm * WTM + i) * 16 + l16;
+    f.a[i] = *reinterpret_cast<const uint4*>(base + r * ROWB + swz<ROWB>(r, chunk) * 16);
+  };
+  auto read_b = [&](Frag& f, const uint8_t* base, auto T, auto J) {
+    constexpr int t = decltype(T)::value, j = decltype(J)::value;
+    const uint8_t* lb = base + A_BYTES + (wn * WTN + j) * BSB;
+    if constexpr (PACKED)
+      rw[j] = *reinterpret_cast<const uint32_t*>(lb + ((q & 1) * 16 + l16) * 16 + (2 * t + (q >> 1)) * 4);
+    else
+      f.b[j] = *reinterpret_cast<const uint4*>(lb + lane * 16);  // whole superblock, piece = lane
+    if constexpr (SCALED && t == 0) {
+      const int col = (wn * WTN + j) * 16 + l16;
+      if constexpr (ZEROS) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4);
+        sc[j] = __builtin_amdgcn_perm(u, u, 0x01000100u);  // low half in both halves
+        zc[j] = __builtin_amdgcn_perm(u, u, 0x03020302u);  // high half in both halves
+      } else {
+        const uint32_t u = *reinterpret_cast<const uint16_t*>(base + A_BYTES + B_BYTES + col * 2);
+        sc[j] = __builtin_amdgcn_perm(u, u, 0x01000100u);
+        zc[j] = 0;
       }
     }
   };
+  auto read_step = [&](Frag& f, int s, auto T) {
+    const uint8_t* base = slot(s);
+    static_for(std::make_integer_sequence<int, WTM>{}, [&](auto I) { read_a(f, base, T, I); });
+    static_for(std::make_integer_sequence<int, WTN>{}, [&](auto J) { read_b(f, base, T, J); });
+  };
 
-  // upcast of column block j from its packed word (int4 / int2 only)
-  auto make_b = [&](Frag& f, int j) {
+  // upcast of word jj of column block j's MFMA operand from its packed word
+  // (int4 / int2 only)
+  auto make_b_part = [&](Frag& f, auto J, auto JJ) {
+    constexpr int j = decltype(J)::value, jj = decltype(JJ)::value;
     if constexpr (PACKED) {
       const uint32_t wd = rw[j];
-      uint32_t o[4];
+      uint32_t o;
       if constexpr (I4) {
         constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          half2v v = as_h2(and_or(wd >> (4 * jj), 0x000F000Fu, 0x64006400u)) - as_h2(bias);
-          if constexpr (ZEROS) v = v - as_h2(zc[j]);
-          if constexpr (SCALED) v = v * as_h2(sc[j]);
-          o[jj] = as_u32(v);
-        }
+        half2v v = as_h2(and_or(wd >> (4 * jj), 0x000F000Fu, 0x64006400u)) - as_h2(bias);
+        if constexpr (ZEROS) v = v - as_h2(zc[j]);
+        if constexpr (SCALED) v = v * as_h2(sc[j]);
+        o = as_u32(v);
+      } else if constexpr (jj < 3) {
+        // offset-binary classes: 0,1,2,3 -> -2,-1,0,1
+        o = __builtin_amdgcn_perm(0u, 0x0100FFFEu, (wd >> (2 * jj)) & 0x03030303u);
       } else {
-#pragma unroll
-        for (int jj = 0; jj < 3; ++jj)  // offset-binary classes: 0,1,2,3 -> -2,-1,0,1
-          o[jj] = __builtin_amdgcn_perm(0u, 0x0100FFFEu, (wd >> (2 * jj)) & 0x03030303u);
         // two's complement class: 0,1,2,3 -> 0,1,-2,-1
-        o[3] = __builtin_amdgcn_perm(0u, 0xFFFE0100u, (wd >> 6) & 0x03030303u);
+        o = __builtin_amdgcn_perm(0u, 0xFFFE0100u, (wd >> 6) & 0x03030303u);
       }
-      f.b[j] = make_uint4(o[0], o[1], o[2], o[3]);
+      // pins the upcast here: otherwise the compiler sinks it into the block of
+      // its first use, past the barrier, where it runs as one serial stretch
+      asm volatile("" : "+v"(o));
+      if constexpr (jj == 0) f.b[j].x = o;
+      else if constexpr (jj == 1) f.b[j].y = o;
+      else if constexpr (jj == 2) f.b[j].z = o;
+      else f.b[j].w = o;
     }
+  };
+  auto make_b = [&](Frag& f, auto J) {
+    static_for(std::make_integer_sequence<int, 4>{}, [&](auto JJ) { make_b_part(f, J, JJ); });
   };
 
   auto mma = [&](const Frag& f, int j) {
@@ -383,12 +419,71 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   // one MFMA step on cur while nxt (already read) is upcast, block by block
   auto compute = [&](const Frag& cur, Frag& nxt) {
     fence();
-#pragma unroll
-    for (int j = 0; j < WTN; ++j) {
-      mma(cur, j);
-      make_b(nxt, j);
-    }
+    static_for(std::make_integer_sequence<int, WTN>{}, [&](auto J) {
+      mma(cur, decltype(J)::value);
+      make_b(nxt, J);
+    });
     fence();
+  };
+
+  // one MFMA (sub-tile i, j)
+  auto mma1 = [&](const Frag& f, auto I, auto J) {
+    constexpr int i = decltype(I)::value, j = decltype(J)::value;
+    if constexpr (FP)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          __builtin_bit_cast(half8v, f.a[i]), __builtin_bit_cast(half8v, f.b[j]), acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+          __builtin_bit_cast(int4v, f.a[i]), __builtin_bit_cast(int4v, f.b[j]), acc[i][j], 0, 0, 0);
+  };
+
+  // Interleaved step (one K group): the MFMAs of cur with, spread evenly between
+  // them in a fixed order, this wave's direct loads of stage st_dma (when DMA),
+  // the fragment reads of step T of the stage in the slot at rb into nxt, and
+  // the upcasts of nxt.  After a barrier the wave thus goes straight back to
+  // MFMAs instead of first issuing its loads and reads in a run, during which
+  // the matrix core of its SIMD would idle.
+  auto step_il = [&](const Frag& cur, Frag& nxt, const uint8_t* rb, auto T, auto DMA, int st_dma) {
+    constexpr bool dma = decltype(DMA)::value;
+    const StageSrc sa = stage_src(dma ? st_dma : 0);
+    constexpr int UPW = ILP == 2 ? 1 : 4;  // upcast side ops per column block
+    constexpr int ND = dma ? NDMA : 0, NU = PACKED ? UPW * WTN : 0;
+    constexpr int NM = WTM * WTN;
+    // With tall wave tiles (16 row fragments) the next activation fragments
+    // cannot be held beside the current ones: fragment i is re-read right after
+    // its last MFMA (column block WTN - 1), and the other side ops are spread
+    // over the MFMAs before that.
+    constexpr bool LATE_A = WTM >= 16 && WTN >= 2;
+    constexpr int NEARLY = LATE_A ? (WTN - 1) * WTM : NM;  // MFMAs that carry the other side ops
+    constexpr int NSIDE = ND + (LATE_A ? 0 : WTM) + WTN + NU;
+    fence();
+    static_for(std::make_integer_sequence<int, NM>{}, [&](auto K) {
+      constexpr int k = decltype(K)::value;
+      mma1(cur, std::integral_constant<int, k % WTM>{}, std::integral_constant<int, k / WTM>{});
+      fence();
+      if constexpr (LATE_A && k >= NEARLY) {
+        read_a(nxt, rb, T, std::integral_constant<int, k - NEARLY>{});
+        fence();
+      } else {
+        constexpr int e0 = k * NSIDE / NEARLY, e1 = (k + 1) * NSIDE / NEARLY;
+        static_for(std::make_integer_sequence<int, e1 - e0>{}, [&](auto E) {
+          constexpr int e = e0 + decltype(E)::value;
+          constexpr int NA = LATE_A ? 0 : WTM;
+          if constexpr (e < ND) dma_one(sa, std::integral_constant<int, e>{});
+          else if constexpr (e < ND + NA) read_a(nxt, rb, T, std::integral_constant<int, e - ND>{});
+          else if constexpr (e < ND + NA + WTN) read_b(nxt, rb, T, std::integral_constant<int, e - ND - NA>{});
+          else if constexpr (UPW == 1) make_b(nxt, std::integral_constant<int, e - ND - NA - WTN>{});
+          else make_b_part(nxt, std::integral_constant<int, (e - ND - NA - WTN) / 4>{},
+                           std::integral_constant<int, (e - ND - NA - WTN) % 4>{});
+          fence();
+        });
+      }
+    });
+  };
+  // waits until round rn's loads have landed everywhere (see sync_round)
+  auto barrier_round = [&] {
+    wait_loads<G::LMIN, G::LMAX, NSTAGE - 2 * KS>(my_loads);
+    asm volatile("s_barrier" ::: "memory");
   };
 
   // prologue: NSTAGE stages in flight, then the fragments of step 0
@@ -399,10 +494,29 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
 
   Frag X, Y;
   read_step(X, kg, std::integral_constant<int, 0>{});
-#pragma unroll
-  for (int j = 0; j < WTN; ++j) make_b(X, j);
+  static_for(std::make_integer_sequence<int, WTN>{}, [&](auto J) { make_b(X, J); });
 
-  if constexpr (NSTEP == 1) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if constexpr (QG_DL_IL && NSTEP == 1) {
+    // one step per stage: each step is preceded by the barrier of the next stage
+    int s = 0;
+    for (; s + 1 < nst; s += 2) {
+      barrier_round();
+      step_il(X, Y, slot(s + 1), I0{}, std::true_type{}, s + NSTAGE);
+      barrier_round();  // past the last stage this reads clamped copies that are never used
+      step_il(Y, X, slot(s + 2), I0{}, std::true_type{}, s + 1 + NSTAGE);
+    }
+    if (s < nst) compute(X, Y);
+  } else if constexpr (QG_DL_IL && ILP != 0 && KS == 1) {
+    // two steps per stage: step 0 reads step 1 of the same stage, step 1 follows
+    // the barrier of the next stage and reads its step 0
+    for (int s = 0; s < nst; ++s) {
+      step_il(X, Y, slot(s), I1{}, std::false_type{}, 0);
+      barrier_round();  // past the last stage this reads clamped copies that are never used
+      step_il(Y, X, slot(s + 1), I0{}, std::true_type{}, s + NSTAGE);
+    }
+  } else if constexpr (NSTEP == 1) {
     // one MFMA step per stage, two stages per iteration
     int s = 0;
     for (; s + 1 < nst; s += 2) {
