@@ -121,6 +121,13 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
   acc_t tot[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) tot[m] = 0;
+  // int2: per-lane sums of the class 0..2 activations (lane l holds dword l of a
+  // superblock's row, class l % 4) over the wave's superblocks; the column-independent
+  // offset-binary correction is taken from them once, after the loop
+  int sacc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) sacc[m] = 0;
+  const int ones012 = (lane & 3) == 3 ? 0 : 0x01010101;
 
   constexpr int UNR = FMT == FMT_I2 ? QG_GEMV_UNR_I2 : QG_GEMV_UNR;
   struct Stage {
@@ -290,11 +297,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
       }
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        // classes 0..2 are offset-binary (q + 2): subtract 2 * (their activation sum)
-        const int mine = (lane & 3) == 3 ? 0 : __builtin_amdgcn_sdot4((int)as[m], 0x01010101, 0, false);
-        const int h = half_wave_sums(mine);
-        const int S012 = lane_value(h, 31) + lane_value(h, 63);
-        tot[m] += acc[0][m] + (acc[1][m] >> 2) + (acc[2][m] >> 4) + (acc[3][m] >> 6) - 2 * S012;
+        sacc[m] = __builtin_amdgcn_sdot4((int)as[m], ones012, sacc[m], false);
+        tot[m] += acc[0][m] + (acc[1][m] >> 2) + (acc[2][m] >> 4) + (acc[3][m] >> 6);
       }
     }
   };
@@ -448,10 +452,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
           });
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        const int mine = (lane & 3) == 3 ? 0 : __builtin_amdgcn_sdot4((int)as[m], 0x01010101, 0, false);
-        const int h = half_wave_sums(mine);
-        const int S012 = lane_value(h, 31) + lane_value(h, 63);
-        tot[m] += acc[0][m] + (acc[1][m] >> 2) + (acc[2][m] >> 4) + (acc[3][m] >> 6) - 2 * S012;
+        sacc[m] = __builtin_amdgcn_sdot4((int)as[m], ones012, sacc[m], false);
+        tot[m] += acc[0][m] + (acc[1][m] >> 2) + (acc[2][m] >> 4) + (acc[3][m] >> 6);
       }
     }
   };
@@ -514,6 +516,15 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
       fence();
       consume(s1, j);
       j += UNR;
+    }
+  }
+
+  if constexpr (FMT == FMT_I2) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      // classes 0..2 are offset-binary (q + 2): subtract 2 * (their activation sum)
+      const int h = half_wave_sums(sacc[m]);
+      tot[m] -= 2 * (lane_value(h, 31) + lane_value(h, 63));
     }
   }
 
