@@ -99,7 +99,8 @@ typedef enum {
  *   k_parts       >= 1: number of contiguous, group-aligned K ranges computed by
  *                 separate workgroups and reduced with fp32/int32 global atomics
  *                 (or two-pass, QGEMM_DETERMINISTIC).  At most K / unit, where
- *                 unit = max(block depth, group_size).
+ *                 unit = group_size when it is a multiple of the block depth
+ *                 (and larger), else the block depth.
  *   flags         0 or QGEMM_DETERMINISTIC.
  *   packed_bytes  out: size of the packed blob for qgemm_pack_weights/qgemm_run.
  *   workspace_bytes out: size of the device workspace qgemm_run needs (0 if none).

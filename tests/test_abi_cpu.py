@@ -74,6 +74,18 @@ def test_create_rejects(kw, status):
     assert _status(**kw) == status
 
 
+@pytest.mark.parametrize("g,K,max_parts", [
+    (128, 4096, 32),    # groups of whole superblocks: one split unit per superblock
+    (512, 4096, 8),     # ... and per group when groups are deeper
+    (-1, 4096, 32),     # one group over K
+    (160, 1920, 15),    # groups that are not whole superblocks (per-piece scales):
+    (96, 1920, 15),     #   parts split at superblocks, not at groups
+])
+def test_split_unit_follows_the_scale_mode(g, K, max_parts):
+    assert _status(group_size=g, K=K, k_parts=max_parts) == q.QGEMM_OK
+    assert _status(group_size=g, K=K, k_parts=max_parts + 1) == q.QGEMM_ERR_INVALID_ARG
+
+
 def test_sizes_and_paths():
     plan, pb, wb = _create()
     assert pb == 4096 * 4096 // 2 + 4096 * 32 * 2 and wb == 0

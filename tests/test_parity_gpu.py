@@ -38,6 +38,16 @@ SMALL = [
     (5, 72, 1024, "i2", 0, False),
     (1, 88, 512, "i4", 64, False),
     (1, 136, 1024, "i4", 0, False),
+    # group sizes that are not whole 128-position superblocks (per-piece scales), and a
+    # deeper group that is not a power of two (its index by division)
+    (1, 300, 1920, "i4", 160, False),
+    (4, 136, 1920, "u4", 96, True),
+    (1, 72, 1920, "u4", 160, True),
+    (1, 200, 1536, "i4", 384, False),
+    (40, 264, 1920, "u4", 160, True),
+    (70, 136, 1920, "i4", 96, False),
+    (40, 264, 1536, "u4", 384, True),
+    (300, 520, 1536, "i4", 384, False),
     # M = 1 with 16-column workgroups at k_parts 1, 64-column blocks at k_parts 3
     (1, 2752, 512, "u4", 128, True),
     (1, 2752, 1024, "i2", 0, False),

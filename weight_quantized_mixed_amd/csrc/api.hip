@@ -96,6 +96,16 @@ int choose_tile(const qgemm_plan* p) {
   return wgs(TILE_128x128) >= 256 ? TILE_128x128 : TILE_64x64;
 }
 
+// Scale mode of a format and group size: per superblock (groups of whole
+// superblocks, or one group over K), else per 32-position piece (groups that
+// are not a multiple of the superblock depth, such as 32, 64, 96 or 160 for int4)
+int scale_mode(int fmt, int32_t group_size) {
+  const int KB = kb_of(fmt);
+  if (group_size == 0) return SC_NONE;
+  if (group_size > 0 && group_size % KB != 0) return SC_PIECE;
+  return SC_BLOCK;
+}
+
 RunArgs make_args(const qgemm_plan* p, const void* A, const void* packed, void* C, void* ws) {
   RunArgs a;
   a.A = A;
@@ -111,7 +121,12 @@ RunArgs make_args(const qgemm_plan* p, const void* A, const void* packed, void* 
   a.nkb = (int32_t)p->L.nkb;
   a.group_size = p->group_size;
   const int KB = kb_of(p->L.fmt);
-  a.smode = p->group_size == 0 ? SC_NONE : (p->group_size > 0 && p->group_size < KB) ? SC_PIECE : SC_BLOCK;
+  a.smode = scale_mode(p->L.fmt, p->group_size);
+  // position -> group as a shift when the group size is a power of two (or one
+  // group spans K), else -1 (divide)
+  a.g_shift = -1;
+  if (p->group_size < 0) a.g_shift = 31;
+  else if (p->group_size > 0 && (p->group_size & (p->group_size - 1)) == 0) a.g_shift = __builtin_ctz(p->group_size);
   a.zeros = p->has_zeros;
   a.k_parts = p->k_parts;
   a.unit_kb = p->unit_kb;
@@ -160,7 +175,8 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   // kernels index the blob with 32-bit uint4 offsets
   if ((N + 255) / 256 * 256 / 16 * (K / KB) * 64 >= INT32_MAX) return QGEMM_ERR_UNSUPPORTED;
 
-  const int64_t unit = group_size > KB ? group_size : KB;
+  // split unit: whole superblocks, and whole groups when groups are whole superblocks
+  const int64_t unit = scale_mode(fmt, group_size) == SC_BLOCK && group_size > KB ? group_size : KB;
   const int64_t n_units = K / unit;
   if (k_parts > n_units) return QGEMM_ERR_INVALID_ARG;
 
@@ -183,8 +199,7 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   p->path = M <= 8 ? QGEMM_PATH_GEMV : QGEMM_PATH_MFMA;
   p->tile = choose_tile(p);
   p->dl_tile = p->path == QGEMM_PATH_MFMA
-                   ? choose_dl_tile(fmt, M, N, k_parts,
-                                    group_size == 0 ? SC_NONE : (group_size > 0 && group_size < KB) ? SC_PIECE : SC_BLOCK)
+                   ? choose_dl_tile(fmt, M, N, k_parts, scale_mode(fmt, group_size))
                    : -1;
   p->gemv_narrow = choose_gemv_narrow(p);
   p->gemv_waves = choose_gemv_waves(p);

@@ -129,6 +129,14 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, T...>, F&&
 #ifndef QG_DL_IL_P_BIG
 #define QG_DL_IL_P_BIG 0
 #endif
+// share (percent) of a step's MFMAs that the side ops are spread over, and
+// whether the fragment reads go before the direct loads (1) or after (0)
+#ifndef QG_DL_IL_SPAN
+#define QG_DL_IL_SPAN 100
+#endif
+#ifndef QG_DL_IL_READS_FIRST
+#define QG_DL_IL_READS_FIRST 0
+#endif
 
 // Stage geometry of a tile configuration.
 template <int FMT, int BM_, int BN_, int WM_, int WN_, int KS_, bool SCALED>
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
     r.dst = lds_off(lds + (st % NSTAGE) * STAGE);
     r.apos = (size_t)pos * ESZ;
     r.sb_row = (size_t)(pos / KB) * a.NB * 1024 + (size_t)(pos % KB) * 1024 / KB;
-    r.grp = SCALED ? pos / (a.group_size > 0 ? a.group_size : a.K) : 0;
+    r.grp = !SCALED ? 0 : a.g_shift >= 0 ? pos >> a.g_shift : pos / a.group_size;
     return r;
   };
   // this wave's direct load e of a stage: A slots, then B slots, then (wave 0) scales
@@ -456,6 +464,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
     constexpr bool LATE_A = WTM >= 16 && WTN >= 2;
     constexpr int NEARLY = LATE_A ? (WTN - 1) * WTM : NM;  // MFMAs that carry the other side ops
     constexpr int NSIDE = ND + (LATE_A ? 0 : WTM) + WTN + NU;
+    constexpr int NCARRY = NEARLY * QG_DL_IL_SPAN / 100 > 0 ? NEARLY * QG_DL_IL_SPAN / 100 : 1;
     fence();
     static_for(std::make_integer_sequence<int, NM>{}, [&](auto K) {
       constexpr int k = decltype(K)::value;
@@ -465,13 +474,21 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
         read_a(nxt, rb, T, std::integral_constant<int, k - NEARLY>{});
         fence();
       } else {
-        constexpr int e0 = k * NSIDE / NEARLY, e1 = (k + 1) * NSIDE / NEARLY;
+        constexpr int e0 = k < NCARRY ? k * NSIDE / NCARRY : NSIDE;
+        constexpr int e1 = k < NCARRY ? (k + 1) * NSIDE / NCARRY : NSIDE;
         static_for(std::make_integer_sequence<int, e1 - e0>{}, [&](auto E) {
           constexpr int e = e0 + decltype(E)::value;
           constexpr int NA = LATE_A ? 0 : WTM;
-          if constexpr (e < ND) dma_one(sa, std::integral_constant<int, e>{});
-          else if constexpr (e < ND + NA) read_a(nxt, rb, T, std::integral_constant<int, e - ND>{});
-          else if constexpr (e < ND + NA + WTN) read_b(nxt, rb, T, std::integral_constant<int, e - ND - NA>{});
+          // side op e: reads (A then B) and direct loads in the chosen order, then upcasts
+          constexpr int RF = QG_DL_IL_READS_FIRST;
+          constexpr int er = RF ? e : e - ND;       // index among the reads
+          constexpr int ed = RF ? e - NA - WTN : e;  // index among the direct loads
+          if constexpr (e < ND + NA + WTN && ((RF && e >= NA + WTN) || (!RF && e < ND)))
+            dma_one(sa, std::integral_constant<int, ed>{});
+          else if constexpr (e < ND + NA + WTN && er < NA)
+            read_a(nxt, rb, T, std::integral_constant<int, er>{});
+          else if constexpr (e < ND + NA + WTN)
+            read_b(nxt, rb, T, std::integral_constant<int, er - NA>{});
           else if constexpr (UPW == 1) make_b(nxt, std::integral_constant<int, e - ND - NA - WTN>{});
           else make_b_part(nxt, std::integral_constant<int, (e - ND - NA - WTN) / 4>{},
                            std::integral_constant<int, (e - ND - NA - WTN) % 4>{});

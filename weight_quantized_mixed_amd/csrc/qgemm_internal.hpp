@@ -80,6 +80,7 @@ struct RunArgs {
   int32_t n_units;      // nkb / unit_kb
   int32_t waves;        // GEMV: waves per workgroup (K split inside the workgroup)
   int32_t sb_per_group; // superblocks per scale group (nkb when one group spans K)
+  int32_t g_shift;      // group of position p = p >> g_shift, or -1: p / group_size
 };
 
 // kernel launchers (return hipSuccess or the launch error)
