@@ -137,6 +137,29 @@ qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const voi
 qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed, void* C,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * C = A . dequant(W) (+ bias) for a run-time number of rows, on `stream`: the
+ * serving form of qgemm_run (decode batches vary from call to call), and the
+ * bias epilogue that BitBLAS's Matmul configuration names with_bias (its
+ * benchmark configurations leave it off; BitBLAS issue #252, reproduction script).
+ *   M          rows this call computes, 1 <= M <= the plan's M, else
+ *              QGEMM_ERR_INVALID_ARG.  The kernels are chosen for this M (as
+ *              qgemm_create would for a plan of M rows); the plan's workspace
+ *              size covers every M.
+ *   A          device, [M, K], as in qgemm_run.
+ *   packed     device, the plan's blob.
+ *   bias       device, [N] of the output type (fp16 or int32), or NULL for none:
+ *              C[m, n] = sum + bias[n].  fp16 outputs add it in fp32 before the
+ *              one rounding to fp16; int32 outputs add it exactly.  Naturally
+ *              aligned (2 / 4 bytes), else QGEMM_ERR_INVALID_ARG.
+ *   C          device, [M, N]; fully overwritten.
+ *   workspace, workspace_bytes, stream: as in qgemm_run.
+ * qgemm_run(plan, A, packed, C, ...) is qgemm_run_ex with the plan's M and no bias.
+ */
+qgemm_status qgemm_run_ex(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,
+                          const void* bias, void* C, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Release a plan; NULL is a no-op.  Device buffers are the caller's. */
 void qgemm_destroy(qgemm_plan* plan);
 

@@ -21,6 +21,10 @@ What is computed, and which passage each step follows:
 * Parallel-k (hidet issue #364 "[Graph][Quantization] Multi-stage software
   pipelining and update parallel k rule": the K dimension split into k-parts
   whose partial products are summed): qgemm_ref_kparts.
+* Optional bias (the with_bias field of the same MatmulConfig, left False in
+  that script's configurations): one value per output column n, added to
+  every row of the product (fp16 bias to the unrounded float64 result, int32
+  bias to the exact integer result).
 
 Precision: dequantisation and accumulation in float64.  Every fp16 value is a
 dyadic rational with an 11-bit significand and every integer weight is below
@@ -96,14 +100,27 @@ def _select_cols(arr, cols):
     return arr if cols is None else arr[np.asarray(cols)]
 
 
+def _add_bias(C, bias, cols, integer: bool):
+    """C[m, n] + bias[n] (bias None -> C unchanged)."""
+    if bias is None:
+        return C
+    b = _select_cols(np.asarray(bias).reshape(-1), cols)
+    if integer:
+        out = C + np.asarray(b, dtype=np.int32).astype(np.int64)[None, :]
+        assert np.all(np.abs(out) < 2**31), "int32 output overflow"
+        return out
+    return C + np.asarray(b, dtype=np.float16).astype(np.float64)[None, :]
+
+
 def qgemm_ref(A, w, s, z, *, N: int, K: int, w_dtype: str, group_size: int,
-              rows=None, cols=None) -> np.ndarray:
-    """Reference result of C = A . dequant(W).
+              rows=None, cols=None, bias=None) -> np.ndarray:
+    """Reference result of C = A . dequant(W) (+ bias).
 
     Returns float64 [M', N'] for fp16 activations (unrounded) and int64 for
     int8 activations (exact; asserted to fit int32).  rows / cols select a
     subset of output rows / columns (sampled tiles of large problems); the
-    other rows and columns are never touched.
+    other rows and columns are never touched.  bias: [N] fp16 (fp16
+    activations) or int32 (int8 activations), or None.
     """
     A = np.asarray(A)
     if rows is not None:
@@ -117,11 +134,11 @@ def qgemm_ref(A, w, s, z, *, N: int, K: int, w_dtype: str, group_size: int,
         C = A.astype(np.float64) @ q.astype(np.float64)
         Ci = np.rint(C).astype(np.int64)
         assert np.all(np.abs(Ci) < 2**31), "int32 accumulator overflow"
-        return Ci
+        return _add_bias(Ci, bias, cols, True)
     s_sel = None if s is None else _select_cols(np.asarray(s).reshape(N, -1), cols)
     z_sel = None if z is None else _select_cols(np.asarray(z).reshape(N, -1), cols)
     W = dequantize(q, s_sel, z_sel, group_size, K)              # [K, n_sel] float64
-    return A.astype(np.float64) @ W
+    return _add_bias(A.astype(np.float64) @ W, bias, cols, False)
 
 
 def k_part_bounds(K: int, group_size: int, k_parts: int, granule: int = 1):
@@ -137,8 +154,8 @@ def k_part_bounds(K: int, group_size: int, k_parts: int, granule: int = 1):
 
 
 def qgemm_ref_kparts(A, w, s, z, *, N: int, K: int, w_dtype: str, group_size: int,
-                     k_parts: int, granule: int = 1) -> np.ndarray:
-    """Parallel-k form: the sum over k-parts of A[:, Kp] . dequant(W)[Kp, :]."""
+                     k_parts: int, granule: int = 1, bias=None) -> np.ndarray:
+    """Parallel-k form: the sum over k-parts of A[:, Kp] . dequant(W)[Kp, :] (+ bias)."""
     A = np.asarray(A)
     q = unpack_weights(w, w_dtype, N, K)
     s_all = None if s is None else np.asarray(s).reshape(N, -1)
@@ -152,7 +169,7 @@ def qgemm_ref_kparts(A, w, s, z, *, N: int, K: int, w_dtype: str, group_size: in
     for k0, k1 in k_part_bounds(K, group_size, k_parts, granule):
         part = A[:, k0:k1].astype(np.float64) @ W[k0:k1]
         acc += np.rint(part).astype(np.int64) if A.dtype == np.int8 else part
-    return acc
+    return _add_bias(acc, bias, None, A.dtype == np.int8)
 
 
 def round_fp16(C64: np.ndarray) -> np.ndarray:

@@ -22,7 +22,7 @@ from typing import Optional
 import numpy as np
 
 # stream ids of the counter-based seed sequence, one per operand
-STREAM_A, STREAM_W, STREAM_S, STREAM_Z = 0, 1, 2, 3
+STREAM_A, STREAM_W, STREAM_S, STREAM_Z, STREAM_B = 0, 1, 2, 3, 4
 
 W_DTYPES = ("i4", "u4", "i2", "i8", "f16")
 A_OF_W = {"i4": "f16", "u4": "f16", "f16": "f16", "i8": "i8", "i2": "i8"}
@@ -110,6 +110,14 @@ def draw_weights(N: int, K: int, w_dtype: str, seed: int) -> np.ndarray:
 def draw_scales(N: int, G: int, seed: int) -> np.ndarray:
     r = _rng(seed, STREAM_S)
     return r.uniform(0.005, 0.02, size=(N, G)).astype(np.float16)
+
+
+def draw_bias(N: int, out_dtype: str, seed: int) -> np.ndarray:
+    """Output bias [N]: fp16 ~ N(0, 1), or int32 uniform over [-2**20, 2**20]."""
+    r = _rng(seed, STREAM_B)
+    if out_dtype == "f16":
+        return r.standard_normal(N).astype(np.float16)
+    return r.integers(-2**20, 2**20 + 1, size=N).astype(np.int32)
 
 
 def draw_zeros(N: int, G: int, seed: int) -> np.ndarray:

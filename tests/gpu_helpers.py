@@ -31,15 +31,21 @@ class Case:
         self.z = host_to_device(p.z)
         self.packed = self.q.pack(self.w, self.s, self.z)
 
-    def run(self):
-        C = self.q.run(self.A, self.packed)
+    def run(self, bias=None, M=None):
+        """qgemm_run, or qgemm_run_ex on the first M rows of A with an optional bias."""
+        if bias is None and M is None:
+            C = self.q.run(self.A, self.packed)
+        else:
+            A = self.A if M is None else self.A[:M]
+            b = None if bias is None else host_to_device(bias)
+            C = self.q.run(A, self.packed, bias=b, M=M)
         torch.cuda.synchronize()
         return C.cpu().numpy()
 
-    def reference(self, rows=None, cols=None):
+    def reference(self, rows=None, cols=None, bias=None):
         p = self.p
         return oracle.qgemm_ref(p.A, p.w, p.s, p.z, N=p.N, K=p.K, w_dtype=p.w_dtype,
-                                group_size=p.group_size, rows=rows, cols=cols)
+                                group_size=p.group_size, rows=rows, cols=cols, bias=bias)
 
 
 def assert_matches(gpu, ref, what=""):

@@ -128,6 +128,24 @@ def test_null_and_misaligned_arguments_rejected_before_launch():
         with pytest.raises(q.QGemmError) as e:
             q.qgemm_pack_weights(plan, 16, 16, 0, 0, 0)        # no output
         assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        # the run-time row count and the bias of qgemm_run_ex (plan M = 1 here)
+        for M in (0, 2, -1):
+            with pytest.raises(q.QGemmError) as e:
+                q.qgemm_run_ex(plan, M, 16, 16, 0, 16, 16, wb, 0)
+            assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_run_ex(plan, 1, 16, 16, 17, 16, 16, wb, 0)  # fp16 bias not 2-byte aligned
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_run_ex(plan, 1, 0, 16, 16, 16, 16, wb, 0)   # no A
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+    finally:
+        q.qgemm_destroy(plan)
+    plan, pb, wb = _create(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0, M=4)
+    try:
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_run_ex(plan, 3, 16, 16, 18, 16, 0, 0, 0)    # int32 bias not 4-byte aligned
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
     finally:
         q.qgemm_destroy(plan)
     assert q.qgemm_plan_path(0) == -1

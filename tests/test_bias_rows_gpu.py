@@ -1,0 +1,81 @@
+"""GPU parity of qgemm_run_ex: the bias epilogue on every path and reduction,
+and run-time row counts below the plan's M, against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import Case, assert_matches, say
+from weight_quantized_mixed_amd import qgemm as q
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _bias(c, seed):
+    return synth.draw_bias(c.p.N, "i32" if c.p.a_dtype == "i8" else "f16", seed)
+
+
+BIAS_CASES = [
+    # M, N, K, w_dtype, g, zeros, k_parts, deterministic
+    (1, 300, 1024, "i4", 128, False, 1, False),    # GEMV, stored
+    (1, 72, 512, "u4", 128, True, 1, False),       # 16-column GEMV
+    (3, 136, 1024, "u4", 64, True, 3, False),      # GEMV, fp32 atomics + finalize
+    (5, 200, 1024, "i8", 0, False, 3, False),      # GEMV, int32 atomics onto the bias rows
+    (5, 200, 2048, "i2", 0, False, 2, True),       # GEMV, two-pass
+    (40, 264, 1024, "i4", 128, False, 1, False),   # direct-load MFMA, stored
+    (64, 72, 1024, "u4", 32, True, 1, False),      # LDS-staged MFMA (per-piece groups)
+    (130, 264, 768, "i4", 64, False, 3, True),     # LDS-staged MFMA, two-pass
+    (129, 136, 512, "i8", 0, False, 3, False),     # direct-load, int32 atomics
+    (300, 520, 512, "f16", 0, False, 2, False),    # direct-load, fp32 atomics
+    (160, 264, 1024, "i2", 0, False, 1, False),    # direct-load int, stored
+]
+
+
+@pytest.mark.parametrize("M,N,K,w_dtype,g,zeros,kp,det", BIAS_CASES)
+def test_bias_epilogue(M, N, K, w_dtype, g, zeros, kp, det):
+    say(f"case bias M={M} N={N} K={K} {w_dtype} g={g} kp={kp} det={det}")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=5000 + M + N)
+    b = _bias(c, 5001 + N)
+    assert_matches(c.run(bias=b), c.reference(bias=b), f"bias M={M} {w_dtype} kp={kp}")
+
+
+ROW_PLANS = [
+    # plan M, N, K, w_dtype, g, zeros, k_parts, deterministic
+    (300, 264, 1024, "i4", 128, False, 1, False),
+    (300, 200, 1024, "u4", 128, True, 2, True),
+    (160, 136, 1024, "i8", 0, False, 3, False),
+    (64, 300, 2048, "i2", 0, False, 1, False),
+    (8, 520, 512, "f16", 0, False, 2, False),
+]
+
+
+@pytest.mark.parametrize("Mp,N,K,w_dtype,g,zeros,kp,det", ROW_PLANS)
+def test_run_time_rows(Mp, N, K, w_dtype, g, zeros, kp, det):
+    say(f"case rows plan M={Mp} N={N} K={K} {w_dtype} kp={kp} det={det}")
+    c = Case(Mp, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=6000 + Mp + N)
+    b = _bias(c, 6001 + N)
+    for M in sorted({1, 2, 5, 8, 9, 33, Mp // 2, Mp}):
+        if M < 1 or M > Mp:
+            continue
+        say(f"  rows M={M}")
+        ref = c.reference(rows=np.arange(M))
+        assert_matches(c.run(M=M), ref, f"rows M={M}/{Mp} {w_dtype}")
+        refb = c.reference(rows=np.arange(M), bias=b)
+        assert_matches(c.run(M=M, bias=b), refb, f"rows+bias M={M}/{Mp} {w_dtype}")
+
+
+def test_run_ex_at_plan_rows_equals_run():
+    c = Case(40, 264, 1024, "i8", 0, False, k_parts=1, seed=7)
+    assert np.array_equal(c.run(), c.run(M=40))
+
+
+def test_run_time_rows_reject_more_than_the_plan():
+    c = Case(4, 72, 512, "i4", 128, False, seed=8)
+    C = torch.empty((5, 72), dtype=torch.float16, device="cuda")
+    A = torch.zeros((5, 512), dtype=torch.float16, device="cuda")
+    with pytest.raises(q.QGemmError) as e:
+        c.q.run(A, c.packed, C=C, M=5)
+    assert e.value.status == q.QGEMM_ERR_INVALID_ARG

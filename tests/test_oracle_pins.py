@@ -53,7 +53,7 @@ def test_encode_unpack_round_trip(w_dtype):
 
 
 # --------------------------------------------------------------------------- brute force
-def _brute(p, kparts=None):
+def _brute(p, kparts=None, bias=None):
     """Exact C by a triple loop over rationals, from the integer weight values."""
     M, N, K, g = p.M, p.N, p.K, p.group_size
     out = [[Fraction(0)] * N for _ in range(M)]
@@ -70,6 +70,8 @@ def _brute(p, kparts=None):
                         wv = wv - Fraction(float(p.z[n, gi]))
                     wv = wv * Fraction(float(p.s[n, gi]))
                 acc += a * wv
+            if bias is not None:
+                acc += Fraction(int(bias[n])) if p.a_dtype == "i8" else Fraction(float(bias[n]))
             out[m][n] = acc
     return out
 
@@ -101,6 +103,40 @@ def test_oracle_vs_exact_brute_force(M, N, K, w_dtype, g, zeros):
             else:
                 # float64 rounding of K products and sums: far below 1e-9 at these sizes
                 assert abs(Fraction(float(C[m, n])) - e) <= Fraction(1, 10**9) * (1 + abs(e)), (m, n)
+
+
+BIAS_CASES = [(3, 7, 128, "i4", 32, False), (2, 5, 128, "u4", -1, True), (2, 9, 256, "i2", 0, False),
+              (3, 6, 64, "i8", 0, False), (2, 5, 64, "f16", 0, False)]
+
+
+@pytest.mark.parametrize("M,N,K,w_dtype,g,zeros", BIAS_CASES)
+def test_oracle_bias_vs_exact_brute_force(M, N, K, w_dtype, g, zeros):
+    p = synth.make_problem(M, N, K, w_dtype, group_size=g, has_zeros=zeros, seed=777 + K + N)
+    b = synth.draw_bias(N, "i32" if p.a_dtype == "i8" else "f16", seed=778 + N)
+    C = oracle.qgemm_ref(p.A, p.w, p.s, p.z, N=N, K=K, w_dtype=w_dtype, group_size=p.group_size, bias=b)
+    exact = _brute(p, bias=b)
+    for m in range(M):
+        for n in range(N):
+            e = exact[m][n]
+            if p.a_dtype == "i8":
+                assert int(C[m, n]) == e, (m, n)
+            else:
+                assert abs(Fraction(float(C[m, n])) - e) <= Fraction(1, 10**9) * (1 + abs(e)), (m, n)
+    # the split-K form adds it once, not once per part
+    Ck = oracle.qgemm_ref_kparts(p.A, p.w, p.s, p.z, N=N, K=K, w_dtype=w_dtype, group_size=p.group_size,
+                                 k_parts=2, granule=32, bias=b)
+    if p.a_dtype == "i8":
+        assert np.array_equal(Ck, C)
+    else:
+        assert np.allclose(Ck, C, rtol=0, atol=1e-9)
+
+
+def test_zero_activations_give_the_bias():
+    N, K = 12, 128
+    p = synth.make_problem(3, N, K, "i4", group_size=128, seed=9)
+    b = synth.draw_bias(N, "f16", seed=10)
+    C = oracle.qgemm_ref(np.zeros_like(p.A), p.w, p.s, p.z, N=N, K=K, w_dtype="i4", group_size=128, bias=b)
+    assert np.array_equal(C, np.broadcast_to(b.astype(np.float64), (3, N)))
 
 
 # --------------------------------------------------------------------------- closed forms
@@ -243,6 +279,8 @@ def _pins_pass():
             test_oracle_vs_exact_brute_force(*c)
         test_one_hot_activation_picks_one_weight("u4", True)
         test_constant_operands_closed_form(True)
+        for c in BIAS_CASES:
+            test_oracle_bias_vs_exact_brute_force(*c)
     except AssertionError:
         return False
     return True
@@ -270,6 +308,17 @@ def _mut_transposed_nibbles(w, w_dtype, N, K):
     return q
 
 
+def _mut_bias_on_rows(C, bias, cols, integer):
+    if bias is None:
+        return C
+    b = np.resize(np.asarray(bias, dtype=np.float64), C.shape[0])
+    return C + (b.astype(np.int64) if integer else b)[:, None]
+
+
+def _mut_bias_dropped(C, bias, cols, integer):
+    return C
+
+
 ORIG_UNPACK = ref.unpack_weights
 ORIG_DEQUANT = ref.dequantize
 
@@ -279,6 +328,8 @@ ORIG_DEQUANT = ref.dequantize
     ("group_index", _mut_group_mod),
     ("dequantize", _mut_zero_dropped),
     ("unpack_weights", _mut_transposed_nibbles),
+    ("_add_bias", _mut_bias_on_rows),
+    ("_add_bias", _mut_bias_dropped),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, target, mutant):
     assert _pins_pass()

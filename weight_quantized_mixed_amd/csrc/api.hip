@@ -10,17 +10,22 @@
 
 using namespace qg;
 
+// the kernels that compute a given number of rows
+struct qg_choice {
+  int path;          // QGEMM_PATH_GEMV or QGEMM_PATH_MFMA
+  int dl_tile;       // direct-load MFMA tile, or -1
+  int tile;          // LDS-staged MFMA tile (used when dl_tile < 0)
+  int gemv_waves;    // GEMV waves per workgroup
+  bool gemv_narrow;  // M = 1 with fewer than 128 blocks of 64 columns: 16-column workgroups
+};
+
 struct qgemm_plan {
   int64_t M, N, K;
   qgemm_dtype a_dtype, w_dtype, out_dtype, accum_dtype;
   int32_t group_size, has_zeros, k_parts;
   uint32_t flags;
   Layout L;
-  int path;          // QGEMM_PATH_GEMV or QGEMM_PATH_MFMA
-  int dl_tile;       // direct-load MFMA tile, or -1
-  int tile;          // LDS-staged MFMA tile (used when dl_tile < 0)
-  int gemv_waves;    // GEMV waves per workgroup
-  bool gemv_narrow;  // M = 1 with fewer than 128 blocks of 64 columns: 16-column workgroups
+  qg_choice ch;      // kernels for M rows (calls with fewer rows choose again)
   int32_t unit_kb, n_units;
   size_t ws_bytes;
 };
@@ -68,12 +73,12 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
 #ifndef QG_GEMV_NARROW_BELOW
 #define QG_GEMV_NARROW_BELOW 128
 #endif
-bool choose_gemv_narrow(const qgemm_plan* p) {
-  return p->path == QGEMM_PATH_GEMV && p->M == 1 && (p->N + 63) / 64 * p->k_parts < QG_GEMV_NARROW_BELOW;
+bool choose_gemv_narrow(const qgemm_plan* p, int64_t M) {
+  return M == 1 && (p->N + 63) / 64 * p->k_parts < QG_GEMV_NARROW_BELOW;
 }
 
-int choose_gemv_waves(const qgemm_plan* p) {
-  const int64_t rb = (p->N + (p->gemv_narrow ? 15 : 63)) / (p->gemv_narrow ? 16 : 64);
+int choose_gemv_waves(const qgemm_plan* p, bool narrow) {
+  const int64_t rb = (p->N + (narrow ? 15 : 63)) / (narrow ? 16 : 64);
   const int64_t per_part = p->L.nkb / p->k_parts;
   int64_t want = (QG_GEMV_TARGET_WAVES + rb * p->k_parts - 1) / (rb * p->k_parts);
   int64_t maxw = per_part / 2;
@@ -85,14 +90,14 @@ int choose_gemv_waves(const qgemm_plan* p) {
 }
 
 // LDS-staged kernel: largest tile that still gives every CU a workgroup (256 CUs).
-int choose_tile(const qgemm_plan* p) {
-  if (p->M <= 32) return TILE_32x64;
+int choose_tile(const qgemm_plan* p, int64_t M) {
+  if (M <= 32) return TILE_32x64;
   auto wgs = [&](int tile) {
     int bm, bn;
     tile_dims(p->L.fmt, tile, &bm, &bn);
-    return ((p->M + bm - 1) / bm) * ((p->N + bn - 1) / bn) * p->k_parts;
+    return ((M + bm - 1) / bm) * ((p->N + bn - 1) / bn) * p->k_parts;
   };
-  if (p->M >= 256 && wgs(TILE_BIG) >= 256) return TILE_BIG;
+  if (M >= 256 && wgs(TILE_BIG) >= 256) return TILE_BIG;
   return wgs(TILE_128x128) >= 256 ? TILE_128x128 : TILE_64x64;
 }
 
@@ -106,14 +111,28 @@ int scale_mode(int fmt, int32_t group_size) {
   return SC_BLOCK;
 }
 
-RunArgs make_args(const qgemm_plan* p, const void* A, const void* packed, void* C, void* ws) {
+qg_choice choose(const qgemm_plan* p, int64_t M) {
+  qg_choice c;
+  c.path = M <= 8 ? QGEMM_PATH_GEMV : QGEMM_PATH_MFMA;
+  c.tile = choose_tile(p, M);
+  c.dl_tile = c.path == QGEMM_PATH_MFMA ? choose_dl_tile(p->L.fmt, M, p->N, p->k_parts,
+                                                          scale_mode(p->L.fmt, p->group_size))
+                                        : -1;
+  c.gemv_narrow = c.path == QGEMM_PATH_GEMV && choose_gemv_narrow(p, M);
+  c.gemv_waves = choose_gemv_waves(p, c.gemv_narrow);
+  return c;
+}
+
+RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const void* A, const void* packed,
+                  const void* bias, void* C, void* ws) {
   RunArgs a;
   a.A = A;
+  a.bias = bias;
   a.W = static_cast<const uint4*>(packed);
   a.S = p->L.G ? static_cast<const char*>(packed) + p->L.s_offset : nullptr;
   a.C = C;
   a.ws = ws;
-  a.M = (int32_t)p->M;
+  a.M = (int32_t)M;
   a.N = (int32_t)p->N;
   a.K = (int32_t)p->K;
   a.Npad = (int32_t)p->L.Npad;
@@ -131,7 +150,7 @@ RunArgs make_args(const qgemm_plan* p, const void* A, const void* packed, void* 
   a.k_parts = p->k_parts;
   a.unit_kb = p->unit_kb;
   a.n_units = p->n_units;
-  a.waves = p->gemv_waves;
+  a.waves = ch.gemv_waves;
   a.sb_per_group = p->group_size > KB ? p->group_size / KB : p->group_size < 0 ? (int32_t)p->L.nkb : 1;
   a.out_mode = p->k_parts == 1 ? OUT_STORE : (p->flags & QGEMM_DETERMINISTIC) ? OUT_PARTIAL : OUT_ATOMIC;
   return a;
@@ -196,13 +215,7 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   fill_layout(&p->L, fmt, N, K, group_size, has_zeros != 0);
   p->unit_kb = (int32_t)(unit / KB);
   p->n_units = (int32_t)n_units;
-  p->path = M <= 8 ? QGEMM_PATH_GEMV : QGEMM_PATH_MFMA;
-  p->tile = choose_tile(p);
-  p->dl_tile = p->path == QGEMM_PATH_MFMA
-                   ? choose_dl_tile(fmt, M, N, k_parts, scale_mode(fmt, group_size))
-                   : -1;
-  p->gemv_narrow = choose_gemv_narrow(p);
-  p->gemv_waves = choose_gemv_waves(p);
+  p->ch = choose(p, M);
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   if (k_parts == 1) p->ws_bytes = 0;
   else if (flags & QGEMM_DETERMINISTIC) p->ws_bytes = mn4 * (size_t)k_parts;
@@ -224,33 +237,44 @@ qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const voi
   return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_DEVICE;
 }
 
-qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed, void* C, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+qgemm_status qgemm_run_ex(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,
+                          const void* bias, void* C, void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan || !A || !packed || !C) return QGEMM_ERR_INVALID_ARG;
+  if (M < 1 || M > plan->M) return QGEMM_ERR_INVALID_ARG;
   if (plan->ws_bytes && (!workspace || workspace_bytes < plan->ws_bytes)) return QGEMM_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(packed) |
        reinterpret_cast<uintptr_t>(workspace)) & 15)
     return QGEMM_ERR_INVALID_ARG;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  RunArgs a = make_args(plan, A, packed, C, workspace);
-  (void)hipGetLastError();  // clear an error left by an unrelated earlier call on this thread
   const bool out_f16 = plan->out_dtype == QGEMM_F16;
+  if (reinterpret_cast<uintptr_t>(bias) & (out_f16 ? 1 : 3)) return QGEMM_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const qg_choice ch = M == plan->M ? plan->ch : choose(plan, M);
+  RunArgs a = make_args(plan, ch, M, A, packed, bias, C, workspace);
+  (void)hipGetLastError();  // clear an error left by an unrelated earlier call on this thread
   hipError_t e = hipSuccess;
   if (a.out_mode == OUT_ATOMIC)
-    e = launch_fill_zero(out_f16 ? workspace : C, (size_t)plan->M * plan->N * 4, st);
+    e = out_f16 ? launch_fill_zero(workspace, (size_t)M * plan->N * 4, st)
+        : bias  ? launch_fill_bias(a, st)
+                : launch_fill_zero(C, (size_t)M * plan->N * 4, st);
   if (e == hipSuccess)
-    e = plan->path == QGEMM_PATH_GEMV ? (plan->gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
-                                                           : launch_gemv(plan->L.fmt, a, st))
-        : plan->dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, plan->dl_tile, a, st)
-        : launch_mfma(plan->L.fmt, plan->tile, a, st);
+    e = ch.path == QGEMM_PATH_GEMV ? (ch.gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
+                                                     : launch_gemv(plan->L.fmt, a, st))
+        : ch.dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, ch.dl_tile, a, st)
+        : launch_mfma(plan->L.fmt, ch.tile, a, st);
   if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))
     e = launch_finalize(a, out_f16, st);
   return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_DEVICE;
 }
 
+qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed, void* C, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!plan) return QGEMM_ERR_INVALID_ARG;
+  return qgemm_run_ex(plan, plan->M, A, packed, nullptr, C, workspace, workspace_bytes, stream);
+}
+
 void qgemm_destroy(qgemm_plan* plan) { delete plan; }
 
-int32_t qgemm_plan_path(const qgemm_plan* plan) { return plan ? plan->path : -1; }
+int32_t qgemm_plan_path(const qgemm_plan* plan) { return plan ? plan->ch.path : -1; }
 
 const char* qgemm_status_string(qgemm_status s) {
   switch (s) {

@@ -541,8 +541,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
     if (col >= a.N) continue;
     const size_t o = (size_t)m * a.N + col;
     if (a.out_mode == OUT_STORE) {
-      if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)s;
-      else static_cast<int*>(a.C)[o] = s;
+      if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)(s + bias_f(a, col));
+      else static_cast<int*>(a.C)[o] = s + bias_i(a, col);
     } else if (a.out_mode == OUT_ATOMIC) {
       if constexpr (FP) unsafeAtomicAdd(static_cast<float*>(a.ws) + o, s);
       else atomicAdd(static_cast<int*>(a.C) + o, s);

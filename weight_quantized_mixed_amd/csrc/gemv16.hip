@@ -166,8 +166,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv16_kernel(RunArgs a) 
       for (int q = 0; q < 4; ++q) s += red[w][q * 16 + threadIdx.x];
     if (col < a.N) {
       if (a.out_mode == OUT_STORE) {
-        if constexpr (FP) static_cast<_Float16*>(a.C)[col] = (_Float16)s;
-        else static_cast<int*>(a.C)[col] = s;
+        if constexpr (FP) static_cast<_Float16*>(a.C)[col] = (_Float16)(s + bias_f(a, col));
+        else static_cast<int*>(a.C)[col] = s + bias_i(a, col);
       } else if (a.out_mode == OUT_ATOMIC) {
         if constexpr (FP) unsafeAtomicAdd(static_cast<float*>(a.ws) + col, s);
         else atomicAdd(static_cast<int*>(a.C) + col, s);

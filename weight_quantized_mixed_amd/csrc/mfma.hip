@@ -258,6 +258,8 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
     for (int j = 0; j < WTN; ++j) {
       const int col = n0 + (wn * WTN + j) * 16 + l16;
       if (col >= a.N) continue;
+      const float bf = FP && a.out_mode == OUT_STORE ? bias_f(a, col) : 0.f;
+      const int bi = !FP && a.out_mode == OUT_STORE ? bias_i(a, col) : 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + (wm * WTM + i) * 16 + kq * 4 + r;
@@ -265,8 +267,8 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
         const size_t o = (size_t)row * a.N + col;
         const auto v = acc[i][j][r];
         if (a.out_mode == OUT_STORE) {
-          if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)v;
-          else static_cast<int*>(a.C)[o] = v;
+          if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)(v + bf);
+          else static_cast<int*>(a.C)[o] = v + bi;
         } else if (a.out_mode == OUT_ATOMIC) {
           if constexpr (FP) unsafeAtomicAdd(static_cast<float*>(a.ws) + o, v);
           else atomicAdd(static_cast<int*>(a.C) + o, v);

@@ -81,7 +81,17 @@ struct RunArgs {
   int32_t waves;        // GEMV: waves per workgroup (K split inside the workgroup)
   int32_t sb_per_group; // superblocks per scale group (nkb when one group spans K)
   int32_t g_shift;      // group of position p = p >> g_shift, or -1: p / group_size
+  const void* bias;     // [N] of the output type, or null
 };
+
+// bias of output column col (0 without bias): fp16 outputs add it in fp32 before
+// their one rounding, int32 outputs exactly
+__device__ __forceinline__ float bias_f(const RunArgs& a, int col) {
+  return a.bias ? (float)static_cast<const _Float16*>(a.bias)[col] : 0.f;
+}
+__device__ __forceinline__ int bias_i(const RunArgs& a, int col) {
+  return a.bias ? static_cast<const int*>(a.bias)[col] : 0;
+}
 
 // kernel launchers (return hipSuccess or the launch error)
 hipError_t launch_pack(const Layout& L, const void* w, const void* s, const void* z, void* packed,
@@ -97,6 +107,8 @@ void dl_tile_dims(int tile, int* bm, int* bn);
 int choose_dl_tile(int fmt, int64_t M, int64_t N, int k_parts, int smode);
 hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// C[m, n] = bias[n] (int32) for the integer atomics to add into
+hipError_t launch_fill_bias(const RunArgs& a, hipStream_t st);
 hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st);
 
 // GEMV tuning: most waves per workgroup (they split the workgroup's K range)

@@ -1,8 +1,9 @@
 // Split-K helpers: zeroing of the atomic accumulator (a fill kernel rather than
-// a memset so that callers may capture qgemm_run in a HIP graph), the fp32 -> fp16
+// a memset so that callers may capture qgemm_run in a HIP graph) or, for int32
+// outputs with a bias, its filling with the bias rows; the fp32 -> fp16
 // conversion after atomic accumulation, and the fixed-order two-pass reduction
 // of per-part partials (the deterministic alternative to the atomic reduction
-// of hidet issue #364's parallel-k).
+// of hidet issue #364's parallel-k), each adding the bias if there is one.
 #include "qgemm_internal.hpp"
 
 namespace qg {
@@ -20,21 +21,30 @@ __global__ void fill_zero_kernel(uint4* __restrict__ p, size_t n16, uint32_t* __
 // conversion after atomics.  Parts are added in order 0, 1, ..., so the result
 // does not depend on scheduling.
 template <bool FP>
-__global__ void finalize_kernel(const void* __restrict__ ws, void* __restrict__ C, size_t mn, int parts) {
+__global__ void finalize_kernel(const void* __restrict__ ws, void* __restrict__ C, size_t mn, int parts,
+                                RunArgs a) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < mn; i += stride) {
+    const int col = a.bias ? (int)(i % (size_t)a.N) : 0;
     if constexpr (FP) {
       const float* w = static_cast<const float*>(ws);
       float s = w[i];
       for (int p = 1; p < parts; ++p) s += w[(size_t)p * mn + i];
-      static_cast<_Float16*>(C)[i] = (_Float16)s;
+      static_cast<_Float16*>(C)[i] = (_Float16)(s + bias_f(a, col));
     } else {
       const int* w = static_cast<const int*>(ws);
       int s = w[i];
       for (int p = 1; p < parts; ++p) s += w[(size_t)p * mn + i];
-      static_cast<int*>(C)[i] = s;
+      static_cast<int*>(C)[i] = s + bias_i(a, col);
     }
   }
+}
+
+// int32 C[m, n] = bias[n], rows of N elements
+__global__ void fill_bias_kernel(int* __restrict__ C, const int* __restrict__ bias, int M, int N) {
+  for (int m = blockIdx.y; m < M; m += gridDim.y)
+    for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < N; n += gridDim.x * blockDim.x)
+      C[(size_t)m * N + n] = bias[n];
 }
 
 int grid_for(size_t items, int threads) {
@@ -59,9 +69,17 @@ hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st) {
   const size_t mn = (size_t)a.M * a.N;
   const int parts = a.out_mode == OUT_PARTIAL ? a.k_parts : 1;
   if (out_f16)
-    hipLaunchKernelGGL(finalize_kernel<true>, dim3(grid_for(mn, 256)), dim3(256), 0, st, a.ws, a.C, mn, parts);
+    hipLaunchKernelGGL(finalize_kernel<true>, dim3(grid_for(mn, 256)), dim3(256), 0, st, a.ws, a.C, mn, parts, a);
   else
-    hipLaunchKernelGGL(finalize_kernel<false>, dim3(grid_for(mn, 256)), dim3(256), 0, st, a.ws, a.C, mn, parts);
+    hipLaunchKernelGGL(finalize_kernel<false>, dim3(grid_for(mn, 256)), dim3(256), 0, st, a.ws, a.C, mn, parts, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_bias(const RunArgs& a, hipStream_t st) {
+  const int gx = (a.N + 255) / 256 < 64 ? (a.N + 255) / 256 : 64;
+  const int gy = a.M < 1024 ? a.M : 1024;
+  hipLaunchKernelGGL(fill_bias_kernel, dim3(gx, gy), dim3(256), 0, st, static_cast<int*>(a.C),
+                     static_cast<const int*>(a.bias), a.M, a.N);
   return hipGetLastError();
 }
 

@@ -73,15 +73,20 @@ class QGemm:
             self._ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         return self._ws
 
-    def new_output(self):
+    def new_output(self, M=None):
         dt = torch.float16 if self.out_dtype == "f16" else torch.int32
-        return torch.empty((self.M, self.N), dtype=dt, device=self.device)
+        return torch.empty((self.M if M is None else int(M), self.N), dtype=dt, device=self.device)
 
-    def run(self, A, packed, C=None, ws=None, stream=None):
+    def run(self, A, packed, C=None, ws=None, stream=None, bias=None, M=None):
+        """C = A . dequant(W) (+ bias[N]) for the plan's M rows, or M <= that."""
         if C is None:
-            C = self.new_output()
+            C = self.new_output(M)
         if ws is None:
             ws = self.workspace()
-        _q.qgemm_run(self.plan, _ptr(A), _ptr(packed), _ptr(C), _ptr(ws),
-                     0 if ws is None else ws.numel(), _stream(stream))
+        wsb = 0 if ws is None else ws.numel()
+        if bias is None and M is None:
+            _q.qgemm_run(self.plan, _ptr(A), _ptr(packed), _ptr(C), _ptr(ws), wsb, _stream(stream))
+        else:
+            _q.qgemm_run_ex(self.plan, self.M if M is None else M, _ptr(A), _ptr(packed), _ptr(bias),
+                            _ptr(C), _ptr(ws), wsb, _stream(stream))
         return C

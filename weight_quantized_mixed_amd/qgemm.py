@@ -21,7 +21,7 @@ QGEMM_OK, QGEMM_ERR_INVALID_ARG, QGEMM_ERR_UNSUPPORTED, QGEMM_ERR_NO_MEMORY, QGE
 QGEMM_DETERMINISTIC = 1
 QGEMM_PATH_GEMV, QGEMM_PATH_MFMA = 1, 2
 
-EXPORTED = ("qgemm_create", "qgemm_pack_weights", "qgemm_run", "qgemm_destroy",
+EXPORTED = ("qgemm_create", "qgemm_pack_weights", "qgemm_run", "qgemm_run_ex", "qgemm_destroy",
             "qgemm_plan_path", "qgemm_status_string")
 
 
@@ -60,6 +60,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qgemm_pack_weights.restype = c_i32
     lib.qgemm_run.argtypes = [c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
     lib.qgemm_run.restype = c_i32
+    lib.qgemm_run_ex.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
+    lib.qgemm_run_ex.restype = c_i32
     lib.qgemm_destroy.argtypes = [c_p]
     lib.qgemm_destroy.restype = None
     lib.qgemm_plan_path.argtypes = [c_p]
@@ -100,6 +102,13 @@ def qgemm_run(plan, A, packed, C, workspace, workspace_bytes, stream=0):
                           int(workspace_bytes), stream or None)
     if st != QGEMM_OK:
         raise QGemmError(st, "qgemm_run")
+
+
+def qgemm_run_ex(plan, M, A, packed, bias, C, workspace, workspace_bytes, stream=0):
+    st = load().qgemm_run_ex(plan, int(M), A or None, packed or None, bias or None, C or None,
+                             workspace or None, int(workspace_bytes), stream or None)
+    if st != QGEMM_OK:
+        raise QGemmError(st, "qgemm_run_ex")
 
 
 def qgemm_destroy(plan):
