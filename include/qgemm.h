@@ -18,6 +18,8 @@
  *   dense : (F16, F16,     F16, F32)
  *   W8A8  : (I8,  I8,      I32, I32)   exact
  *   W2A8  : (I8,  I2,      I32, I32)   exact
+ *   W8A8 / W2A8 dequantised: (I8, I8 | I2, F16, I32), run with per-row and
+ *           per-column fp32 scales through qgemm_run_scaled
  * Any other tuple returns QGEMM_ERR_UNSUPPORTED (fp16 accumulation and int8
  * output are not provided: the int8 narrowing rule is unspecified).
  *
@@ -159,6 +161,43 @@ qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed
 qgemm_status qgemm_run_ex(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,
                           const void* bias, void* C, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * int8 activations with fp16 output (plans created with the tuple
+ * (I8, I8 | I2, F16, I32)): C[m, n] = fp16(acc[m, n] * row_scales[m] *
+ * col_scales[n] (+ bias[n])), the dequantising epilogue of the int8
+ * dynamic-activation configurations (torchao issue #2752), computed in fp32
+ * from the exact int32 accumulator with one rounding.  Such plans run only
+ * through this call (qgemm_run / qgemm_run_ex return QGEMM_ERR_INVALID_ARG).
+ *   M          rows, 1 <= M <= the plan's M.
+ *   A          device, int8 [M, K] (e.g. from qgemm_quantize_rows).
+ *   row_scales device, fp32 [M] (per-token activation scales).
+ *   col_scales device, fp32 [N] (per-channel weight scales).
+ *   bias       device, fp16 [N], or NULL.
+ *   C          device, fp16 [M, N]; fully overwritten.
+ *   workspace, workspace_bytes, stream: as in qgemm_run.
+ */
+qgemm_status qgemm_run_scaled(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,
+                              const float* row_scales, const float* col_scales, const void* bias,
+                              void* C, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dynamic per-token int8 quantisation of fp16 activations (the activation step
+ * of torchao issue #2752's Int8DynamicActivation* configurations), symmetric
+ * with one scale per row:
+ *   scales[m] = max_k |A[m, k]| / 127                  (fp32, round to nearest)
+ *   Q[m, k]   = clamp(rint(A[m, k] / scales[m]), -127, 127)
+ * with the division in fp32, correctly rounded, rint to nearest even; an
+ * all-zero row gets scale 0 and codes 0.
+ *   A       device, fp16 [M, K], 16-byte aligned.
+ *   M, K    M >= 1; K >= 8 and a multiple of 8.
+ *   Q       device, int8 [M, K], 8-byte aligned; fully overwritten.
+ *   scales  device, fp32 [M], 4-byte aligned; fully overwritten.
+ * Asynchronous on `stream`.  QGEMM_ERR_INVALID_ARG on a bad argument (checked
+ * before any launch), QGEMM_ERR_DEVICE if the launch fails.
+ */
+qgemm_status qgemm_quantize_rows(const void* A, int64_t M, int64_t K, void* Q, float* scales,
+                                 void* stream);
 
 /* Release a plan; NULL is a no-op.  Device buffers are the caller's. */
 void qgemm_destroy(qgemm_plan* plan);

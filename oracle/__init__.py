@@ -7,5 +7,5 @@ It shares no code with the GPU path.
 """
 from .core import (  # noqa: F401
     unpack_weights, dequantize, k_part_bounds, qgemm_ref, qgemm_ref_kparts,
-    round_fp16, fp16_within_tol, group_index, FP16_ATOL, FP16_RTOL,
+    round_fp16, fp16_within_tol, group_index, FP16_ATOL, FP16_RTOL, quantize_rows, qgemm_ref_scaled,
 )

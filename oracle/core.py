@@ -21,6 +21,10 @@ What is computed, and which passage each step follows:
 * Parallel-k (hidet issue #364 "[Graph][Quantization] Multi-stage software
   pipelining and update parallel k rule": the K dimension split into k-parts
   whose partial products are summed): qgemm_ref_kparts.
+* Dynamic per-token int8 quantisation of fp16 activations and the fp16 output
+  of the int8 products dequantised with per-row and per-column scales
+  (torchao issue #2752, Int8DynamicActivation* configurations): quantize_rows,
+  qgemm_ref_scaled.
 * Optional bias (the with_bias field of the same MatmulConfig, left False in
   that script's configurations): one value per output column n, added to
   every row of the product (fp16 bias to the unrounded float64 result, int32
@@ -170,6 +174,40 @@ def qgemm_ref_kparts(A, w, s, z, *, N: int, K: int, w_dtype: str, group_size: in
         part = A[:, k0:k1].astype(np.float64) @ W[k0:k1]
         acc += np.rint(part).astype(np.int64) if A.dtype == np.int8 else part
     return _add_bias(acc, bias, None, A.dtype == np.int8)
+
+
+def quantize_rows(A) -> tuple[np.ndarray, np.ndarray]:
+    """Dynamic per-token symmetric int8 quantisation of fp16 activations [M, K].
+
+    The activation step of the int8 dynamic-activation configurations (torchao
+    issue #2752: Int8DynamicActivationInt8WeightConfig,
+    Int8DynamicActivationIntxWeightConfig).  The pages name the scheme, not its
+    arithmetic; the reading taken here: one symmetric scale per row,
+    scale = max|a| / 127 in fp32 (rounded to nearest), codes
+    rint(a / scale) (fp32 division, ties to even) clamped to [-127, 127], and
+    scale 0 with codes 0 for an all-zero row.  Returns (int8 [M, K], fp32 [M]).
+    """
+    A32 = np.asarray(A, dtype=np.float16).astype(np.float32)
+    amax = np.max(np.abs(A32), axis=1)                        # exact
+    scale = (amax / np.float32(127)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
+    codes = np.rint((A32 / safe[:, None]).astype(np.float32))
+    codes = np.where(scale[:, None] > 0, np.clip(codes, -127, 127), 0)
+    return codes.astype(np.int8), scale
+
+
+def qgemm_ref_scaled(Aq, w, *, N: int, K: int, w_dtype: str, row_scales, col_scales, bias=None,
+                     rows=None, cols=None) -> np.ndarray:
+    """fp16-output form of the int8 products: acc[m, n] * row_scales[m] *
+    col_scales[n] (+ bias[n]), from the exact int32 accumulator, unrounded
+    float64 (the dequantising step after an int8 x int8 / int2 product with
+    per-token activation and per-channel weight scales)."""
+    acc = qgemm_ref(Aq, w, None, None, N=N, K=K, w_dtype=w_dtype, group_size=0, rows=rows, cols=cols)
+    rs = np.asarray(row_scales, dtype=np.float32).astype(np.float64)
+    if rows is not None:
+        rs = rs[np.asarray(rows)]
+    cs = _select_cols(np.asarray(col_scales, dtype=np.float32).astype(np.float64), cols)
+    return _add_bias(acc.astype(np.float64) * rs[:, None] * cs[None, :], bias, cols, False)
 
 
 def round_fp16(C64: np.ndarray) -> np.ndarray:

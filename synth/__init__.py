@@ -22,7 +22,7 @@ from typing import Optional
 import numpy as np
 
 # stream ids of the counter-based seed sequence, one per operand
-STREAM_A, STREAM_W, STREAM_S, STREAM_Z, STREAM_B = 0, 1, 2, 3, 4
+STREAM_A, STREAM_W, STREAM_S, STREAM_Z, STREAM_B, STREAM_C = 0, 1, 2, 3, 4, 5
 
 W_DTYPES = ("i4", "u4", "i2", "i8", "f16")
 A_OF_W = {"i4": "f16", "u4": "f16", "f16": "f16", "i8": "i8", "i2": "i8"}
@@ -118,6 +118,16 @@ def draw_bias(N: int, out_dtype: str, seed: int) -> np.ndarray:
     if out_dtype == "f16":
         return r.standard_normal(N).astype(np.float16)
     return r.integers(-2**20, 2**20 + 1, size=N).astype(np.int32)
+
+
+def draw_col_scales(N: int, seed: int) -> np.ndarray:
+    """Per-channel fp32 weight scales [N], uniform over [0.001, 0.01]."""
+    return _rng(seed, STREAM_C).uniform(0.001, 0.01, size=N).astype(np.float32)
+
+
+def draw_fp16_activations(M: int, K: int, seed: int) -> np.ndarray:
+    """fp16 [M, K] ~ N(0, 1) (the activations that the int8 quantiser reads)."""
+    return draw_activations(M, K, "f16", seed)
 
 
 def draw_zeros(N: int, G: int, seed: int) -> np.ndarray:

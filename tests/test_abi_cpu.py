@@ -42,7 +42,9 @@ def _status(**kw):
 def test_create_valid_formats():
     for kw in [dict(), dict(w_dtype="u4", has_zeros=1), dict(w_dtype="f16", group_size=0),
                dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0),
-               dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=0)]:
+               dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=0),
+               dict(a_dtype="i8", w_dtype="i8", out_dtype="f16", accum_dtype="i32", group_size=0),
+               dict(a_dtype="i8", w_dtype="i2", out_dtype="f16", accum_dtype="i32", group_size=0)]:
         assert _status(**kw) == q.QGEMM_OK, kw
 
 
@@ -150,6 +152,31 @@ def test_null_and_misaligned_arguments_rejected_before_launch():
         q.qgemm_destroy(plan)
     assert q.qgemm_plan_path(0) == -1
     q.qgemm_destroy(0)                                         # NULL is a no-op
+    # dequantised int8 plans run only with their scales, other plans never with scales
+    dq, _, wb = _create(a_dtype="i8", w_dtype="i8", out_dtype="f16", accum_dtype="i32", group_size=0,
+                        M=4, k_parts=2)
+    i32, _, _ = _create(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0, M=4)
+    try:
+        assert wb == 4 * 4096 * 4                              # int32 atomics go to the workspace
+        for call in [lambda: q.qgemm_run(dq, 16, 16, 16, 16, wb, 0),
+                     lambda: q.qgemm_run_ex(dq, 4, 16, 16, 0, 16, 16, wb, 0),
+                     lambda: q.qgemm_run_scaled(dq, 4, 16, 16, 0, 16, 0, 16, 16, wb, 0),   # no row scales
+                     lambda: q.qgemm_run_scaled(dq, 4, 16, 16, 16, 0, 0, 16, 16, wb, 0),   # no column scales
+                     lambda: q.qgemm_run_scaled(dq, 4, 16, 16, 18, 16, 0, 16, 16, wb, 0),  # misaligned
+                     lambda: q.qgemm_run_scaled(dq, 5, 16, 16, 16, 16, 0, 16, 16, wb, 0),  # M > plan M
+                     lambda: q.qgemm_run_scaled(i32, 4, 16, 16, 16, 16, 0, 16, 0, 0, 0)]:   # int32 plan
+            with pytest.raises(q.QGemmError) as e:
+                call()
+            assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+    finally:
+        q.qgemm_destroy(dq)
+        q.qgemm_destroy(i32)
+    for args in [(0, 4, 64, 16, 16), (16, 0, 64, 16, 16), (16, 4, 60, 16, 16), (16, 4, 0, 16, 16),
+                 (18, 4, 64, 16, 16), (16, 4, 64, 20, 16), (16, 4, 64, 16, 18), (16, 4, 64, 0, 16),
+                 (16, 4, 64, 16, 0)]:
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_quantize_rows(args[0], args[1], args[2], args[3], args[4], 0)
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG, args
     assert q.qgemm_status_string(2) == "unsupported format or shape"
 
 

@@ -7,6 +7,7 @@ weights, identity weights, one-hot activations, constant operands), the
 parallel-k decomposition, and exact invariants.  A last group of tests plants
 plausible mistakes in a copy of the oracle and checks that a pin catches each.
 """
+import struct
 from fractions import Fraction
 
 import numpy as np
@@ -336,3 +337,106 @@ def test_planted_mistakes_are_caught(monkeypatch, target, mutant):
     monkeypatch.setattr(ref, target, mutant)
     monkeypatch.setattr(oracle, target, mutant, raising=False)
     assert not _pins_pass()
+
+
+# --------------------------------------------------------------------------- int8 activation quantiser
+def _f32(x: float) -> float:
+    """Round a Python float (binary64) to the nearest binary32 value."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def _quantize_loop(A):
+    """Per-row codes and scales by plain loops: binary64 division then one
+    rounding to binary32 is the correctly rounded binary32 quotient of binary32
+    operands, and Python's round() takes ties to even."""
+    codes, scales = [], []
+    for row in np.asarray(A, dtype=np.float16).tolist():
+        amax = max(abs(float(v)) for v in row)
+        s = _f32(amax / 127.0)
+        scales.append(s)
+        if s == 0.0:
+            codes.append([0] * len(row))
+            continue
+        codes.append([max(-127, min(127, round(_f32(float(v) / s)))) for v in row])
+    return codes, scales
+
+
+def test_quantize_rows_matches_loops():
+    A = synth.draw_fp16_activations(6, 96, seed=31)
+    A[2] *= np.float16(1e-3)   # small magnitudes
+    A[3] = 0                   # all-zero row
+    A[4, 7] = np.float16(-60000)  # one dominant value
+    q, s = oracle.quantize_rows(A)
+    qc, sc = _quantize_loop(A)
+    assert s.dtype == np.float32 and q.dtype == np.int8
+    assert [float(v) for v in s] == sc
+    assert q.tolist() == qc
+
+
+def test_quantize_rows_closed_forms():
+    # exact multiples of a power-of-two scale map to their multipliers
+    row = np.array([0, 1, -2, 127, -127, 64], dtype=np.float16) / np.float16(64)
+    q, s = oracle.quantize_rows(row[None, :])
+    assert s[0] == np.float32(1 / 64) and q[0].tolist() == [0, 1, -2, 127, -127, 64]
+    # ties go to even: scale 2, quotients 0.5, 1.5, 2.5, -2.5 -> 0, 2, 2, -2
+    q, s = oracle.quantize_rows(np.array([[254, 1, 3, 5, -5]], dtype=np.float16))
+    assert s[0] == 2 and q[0].tolist() == [127, 0, 2, 2, -2]
+    # an all-zero row: scale 0, codes 0
+    q, s = oracle.quantize_rows(np.zeros((1, 8), dtype=np.float16))
+    assert s[0] == 0 and not q.any()
+
+
+def test_quantize_rows_error_bound():
+    A = synth.draw_fp16_activations(16, 256, seed=32)
+    q, s = oracle.quantize_rows(A)
+    err = np.abs(A.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+    # half a step, plus the fp32 rounding of the scale and the quotient
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+    assert np.all(np.abs(q.astype(np.int64)).max(axis=1) == 127)
+
+
+def test_scaled_products_vs_exact_brute_force():
+    M, N, K = 3, 5, 128
+    for w_dtype in ("i8", "i2"):
+        p = synth.make_problem(M, N, K if w_dtype == "i8" else 256, w_dtype, group_size=0, seed=41)
+        rs = synth.draw_col_scales(M, seed=42)          # any positive fp32 values serve as row scales
+        cs = synth.draw_col_scales(N, seed=43)
+        b = synth.draw_bias(N, "f16", seed=44)
+        C = oracle.qgemm_ref_scaled(p.A, p.w, N=N, K=p.K, w_dtype=w_dtype, row_scales=rs, col_scales=cs, bias=b)
+        exact = _brute(p)
+        for m in range(M):
+            for n in range(N):
+                e = exact[m][n] * Fraction(float(rs[m])) * Fraction(float(cs[n])) + Fraction(float(b[n]))
+                assert abs(Fraction(float(C[m, n])) - e) <= Fraction(1, 10**9) * (1 + abs(e)), (w_dtype, m, n)
+
+
+def _mut_round_half_away(A):
+    A32 = np.asarray(A, dtype=np.float16).astype(np.float32)
+    amax = np.max(np.abs(A32), axis=1)
+    scale = (amax / np.float32(127)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
+    x = (A32 / safe[:, None]).astype(np.float32)
+    codes = np.sign(x) * np.floor(np.abs(x) + 0.5)
+    return np.where(scale[:, None] > 0, np.clip(codes, -127, 127), 0).astype(np.int8), scale
+
+
+def _mut_scale_128(A):
+    A32 = np.asarray(A, dtype=np.float16).astype(np.float32)
+    scale = (np.max(np.abs(A32), axis=1) / np.float32(128)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
+    codes = np.rint((A32 / safe[:, None]).astype(np.float32))
+    return np.where(scale[:, None] > 0, np.clip(codes, -127, 127), 0).astype(np.int8), scale
+
+
+@pytest.mark.parametrize("mutant", [_mut_round_half_away, _mut_scale_128])
+def test_quantizer_planted_mistakes_are_caught(monkeypatch, mutant):
+    def pins():
+        try:
+            test_quantize_rows_matches_loops()
+            test_quantize_rows_closed_forms()
+        except AssertionError:
+            return False
+        return True
+    assert pins()
+    monkeypatch.setattr(oracle, "quantize_rows", mutant)
+    assert not pins()

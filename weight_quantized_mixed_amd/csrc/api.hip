@@ -128,6 +128,8 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
   RunArgs a;
   a.A = A;
   a.bias = bias;
+  a.row_scale = nullptr;
+  a.col_scale = nullptr;
   a.W = static_cast<const uint4*>(packed);
   a.S = p->L.G ? static_cast<const char*>(packed) + p->L.s_offset : nullptr;
   a.C = C;
@@ -158,6 +160,48 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
 
 }  // namespace
 
+namespace {
+
+// one run: the split-K fill, the kernel chosen for M rows, the finalize pass
+qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const void* packed, const void* bias,
+                      const float* row_scales, const float* col_scales, void* C, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!plan || !A || !packed || !C) return QGEMM_ERR_INVALID_ARG;
+  if (M < 1 || M > plan->M) return QGEMM_ERR_INVALID_ARG;
+  if (plan->ws_bytes && (!workspace || workspace_bytes < plan->ws_bytes)) return QGEMM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(packed) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return QGEMM_ERR_INVALID_ARG;
+  const bool out_f16 = plan->out_dtype == QGEMM_F16;
+  const bool acc_fp = plan->a_dtype == QGEMM_F16;
+  if (reinterpret_cast<uintptr_t>(bias) & (out_f16 ? 1 : 3)) return QGEMM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(row_scales) | reinterpret_cast<uintptr_t>(col_scales)) & 3)
+    return QGEMM_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const qg_choice ch = M == plan->M ? plan->ch : choose(plan, M);
+  RunArgs a = make_args(plan, ch, M, A, packed, bias, C, workspace);
+  a.row_scale = row_scales;
+  a.col_scale = col_scales;
+  (void)hipGetLastError();  // clear an error left by an unrelated earlier call on this thread
+  hipError_t e = hipSuccess;
+  if (a.out_mode == OUT_ATOMIC)
+    e = out_f16 ? launch_fill_zero(workspace, (size_t)M * plan->N * 4, st)  // fp32 / int32 accumulator
+        : bias  ? launch_fill_bias(a, st)
+                : launch_fill_zero(C, (size_t)M * plan->N * 4, st);
+  if (e == hipSuccess)
+    e = ch.path == QGEMM_PATH_GEMV ? (ch.gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
+                                                     : launch_gemv(plan->L.fmt, a, st))
+        : ch.dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, ch.dl_tile, a, st)
+        : launch_mfma(plan->L.fmt, ch.tile, a, st);
+  if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))
+    e = launch_finalize(a, acc_fp, st);
+  return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_DEVICE;
+}
+
+bool dequant_plan(const qgemm_plan* p) { return p->a_dtype == QGEMM_I8 && p->out_dtype == QGEMM_F16; }
+
+}  // namespace
+
 extern "C" {
 
 qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qgemm_dtype a_dtype,
@@ -178,8 +222,10 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   // legal format tuples
   const bool fp_tuple = a_dtype == QGEMM_F16 && out_dtype == QGEMM_F16 && accum_dtype == QGEMM_F32 &&
                         (w_dtype == QGEMM_I4 || w_dtype == QGEMM_U4 || w_dtype == QGEMM_F16);
-  const bool int_tuple = a_dtype == QGEMM_I8 && out_dtype == QGEMM_I32 && accum_dtype == QGEMM_I32 &&
-                         (w_dtype == QGEMM_I8 || w_dtype == QGEMM_I2);
+  // int8 activations: int32 output, or fp16 output dequantised with per-row and
+  // per-column scales (qgemm_run_scaled)
+  const bool int_tuple = a_dtype == QGEMM_I8 && (out_dtype == QGEMM_I32 || out_dtype == QGEMM_F16) &&
+                         accum_dtype == QGEMM_I32 && (w_dtype == QGEMM_I8 || w_dtype == QGEMM_I2);
   if (!fp_tuple && !int_tuple) return QGEMM_ERR_UNSUPPORTED;
   const int fmt = fmt_of(w_dtype);
   const int KB = kb_of(fmt);
@@ -219,7 +265,7 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   if (k_parts == 1) p->ws_bytes = 0;
   else if (flags & QGEMM_DETERMINISTIC) p->ws_bytes = mn4 * (size_t)k_parts;
-  else p->ws_bytes = out_dtype == QGEMM_F16 ? mn4 : 0;
+  else p->ws_bytes = out_dtype == QGEMM_F16 ? mn4 : 0;  // int32 output: atomics straight into C
   if (packed_bytes) *packed_bytes = p->L.total;
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
   *out = p;
@@ -239,30 +285,24 @@ qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const voi
 
 qgemm_status qgemm_run_ex(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,
                           const void* bias, void* C, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!plan || !A || !packed || !C) return QGEMM_ERR_INVALID_ARG;
-  if (M < 1 || M > plan->M) return QGEMM_ERR_INVALID_ARG;
-  if (plan->ws_bytes && (!workspace || workspace_bytes < plan->ws_bytes)) return QGEMM_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(packed) |
-       reinterpret_cast<uintptr_t>(workspace)) & 15)
+  if (!plan || dequant_plan(plan)) return QGEMM_ERR_INVALID_ARG;  // those need their scales
+  return run_impl(plan, M, A, packed, bias, nullptr, nullptr, C, workspace, workspace_bytes, stream);
+}
+
+qgemm_status qgemm_run_scaled(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,
+                              const float* row_scales, const float* col_scales, const void* bias, void* C,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !dequant_plan(plan) || !row_scales || !col_scales) return QGEMM_ERR_INVALID_ARG;
+  return run_impl(plan, M, A, packed, bias, row_scales, col_scales, C, workspace, workspace_bytes, stream);
+}
+
+qgemm_status qgemm_quantize_rows(const void* A, int64_t M, int64_t K, void* Q, float* scales, void* stream) {
+  if (!A || !Q || !scales || M < 1 || K < 8 || K % 8 != 0) return QGEMM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(Q) & 7) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3))
     return QGEMM_ERR_INVALID_ARG;
-  const bool out_f16 = plan->out_dtype == QGEMM_F16;
-  if (reinterpret_cast<uintptr_t>(bias) & (out_f16 ? 1 : 3)) return QGEMM_ERR_INVALID_ARG;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const qg_choice ch = M == plan->M ? plan->ch : choose(plan, M);
-  RunArgs a = make_args(plan, ch, M, A, packed, bias, C, workspace);
-  (void)hipGetLastError();  // clear an error left by an unrelated earlier call on this thread
-  hipError_t e = hipSuccess;
-  if (a.out_mode == OUT_ATOMIC)
-    e = out_f16 ? launch_fill_zero(workspace, (size_t)M * plan->N * 4, st)
-        : bias  ? launch_fill_bias(a, st)
-                : launch_fill_zero(C, (size_t)M * plan->N * 4, st);
-  if (e == hipSuccess)
-    e = ch.path == QGEMM_PATH_GEMV ? (ch.gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
-                                                     : launch_gemv(plan->L.fmt, a, st))
-        : ch.dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, ch.dl_tile, a, st)
-        : launch_mfma(plan->L.fmt, ch.tile, a, st);
-  if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))
-    e = launch_finalize(a, out_f16, st);
+  (void)hipGetLastError();
+  hipError_t e = launch_quantize_rows(A, M, K, Q, scales, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_DEVICE;
 }
 

@@ -542,10 +542,11 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
     const size_t o = (size_t)m * a.N + col;
     if (a.out_mode == OUT_STORE) {
       if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)(s + bias_f(a, col));
+      else if (a.row_scale) static_cast<_Float16*>(a.C)[o] = dq_out(a, m, col, s);
       else static_cast<int*>(a.C)[o] = s + bias_i(a, col);
     } else if (a.out_mode == OUT_ATOMIC) {
       if constexpr (FP) unsafeAtomicAdd(static_cast<float*>(a.ws) + o, s);
-      else atomicAdd(static_cast<int*>(a.C) + o, s);
+      else atomicAdd(int_atomic_target(a) + o, s);
     } else {
       static_cast<acc_t*>(a.ws)[(size_t)part * a.M * a.N + o] = s;
     }

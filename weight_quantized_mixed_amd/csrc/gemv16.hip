@@ -167,10 +167,11 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv16_kernel(RunArgs a) 
     if (col < a.N) {
       if (a.out_mode == OUT_STORE) {
         if constexpr (FP) static_cast<_Float16*>(a.C)[col] = (_Float16)(s + bias_f(a, col));
+        else if (a.row_scale) static_cast<_Float16*>(a.C)[col] = dq_out(a, 0, col, s);
         else static_cast<int*>(a.C)[col] = s + bias_i(a, col);
       } else if (a.out_mode == OUT_ATOMIC) {
         if constexpr (FP) unsafeAtomicAdd(static_cast<float*>(a.ws) + col, s);
-        else atomicAdd(static_cast<int*>(a.C) + col, s);
+        else atomicAdd(int_atomic_target(a) + col, s);
       } else {
         static_cast<acc_t*>(a.ws)[(size_t)part * a.N + col] = s;
       }

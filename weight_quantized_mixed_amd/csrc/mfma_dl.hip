@@ -604,10 +604,11 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
         const auto v = acc[i][j][r];
         if (a.out_mode == OUT_STORE) {
           if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)(v + bf);
+          else if (a.row_scale) static_cast<_Float16*>(a.C)[o] = dq_out(a, row, col, v);
           else static_cast<int*>(a.C)[o] = v + bi;
         } else if (a.out_mode == OUT_ATOMIC) {
           if constexpr (FP) unsafeAtomicAdd(static_cast<float*>(a.ws) + o, v);
-          else atomicAdd(static_cast<int*>(a.C) + o, v);
+          else atomicAdd(int_atomic_target(a) + o, v);
         } else {
           if constexpr (FP) static_cast<float*>(a.ws)[(size_t)part * a.M * a.N + o] = v;
           else static_cast<int*>(a.ws)[(size_t)part * a.M * a.N + o] = v;

@@ -82,6 +82,10 @@ struct RunArgs {
   int32_t sb_per_group; // superblocks per scale group (nkb when one group spans K)
   int32_t g_shift;      // group of position p = p >> g_shift, or -1: p / group_size
   const void* bias;     // [N] of the output type, or null
+  // int8 activations with fp16 output: C = fp16(acc * row_scale[m] * col_scale[n]
+  // (+ bias)); null for int32 output
+  const float* row_scale;
+  const float* col_scale;
 };
 
 // bias of output column col (0 without bias): fp16 outputs add it in fp32 before
@@ -91,6 +95,16 @@ __device__ __forceinline__ float bias_f(const RunArgs& a, int col) {
 }
 __device__ __forceinline__ int bias_i(const RunArgs& a, int col) {
   return a.bias ? static_cast<const int*>(a.bias)[col] : 0;
+}
+// fp16 output of an int32 accumulator: the per-row (activation) and per-column
+// (weight) scales and the bias applied in fp32, one rounding to fp16
+__device__ __forceinline__ _Float16 dq_out(const RunArgs& a, int row, int col, int acc) {
+  return (_Float16)((float)acc * a.row_scale[row] * a.col_scale[col] + bias_f(a, col));
+}
+// where integer split-K atomics add up: C itself, or the workspace when the
+// output is dequantised afterwards
+__device__ __forceinline__ int* int_atomic_target(const RunArgs& a) {
+  return static_cast<int*>(a.row_scale ? a.ws : a.C);
 }
 
 // kernel launchers (return hipSuccess or the launch error)
@@ -109,7 +123,11 @@ hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // C[m, n] = bias[n] (int32) for the integer atomics to add into
 hipError_t launch_fill_bias(const RunArgs& a, hipStream_t st);
-hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st);
+// per-row symmetric int8 quantisation of fp16 activations (quant.hip)
+hipError_t launch_quantize_rows(const void* A, int64_t M, int64_t K, void* Q, float* scales, hipStream_t st);
+// sums the per-part partials (or converts the atomic accumulator) into C;
+// acc_fp: fp32 accumulator (fp16 activations), else int32
+hipError_t launch_finalize(const RunArgs& a, int acc_fp, hipStream_t st);
 
 // GEMV tuning: most waves per workgroup (they split the workgroup's K range)
 // and superblocks per register stage

@@ -25,7 +25,7 @@ __global__ void finalize_kernel(const void* __restrict__ ws, void* __restrict__ 
                                 RunArgs a) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < mn; i += stride) {
-    const int col = a.bias ? (int)(i % (size_t)a.N) : 0;
+    const int col = (a.bias || a.row_scale) ? (int)(i % (size_t)a.N) : 0;
     if constexpr (FP) {
       const float* w = static_cast<const float*>(ws);
       float s = w[i];
@@ -35,7 +35,8 @@ __global__ void finalize_kernel(const void* __restrict__ ws, void* __restrict__ 
       const int* w = static_cast<const int*>(ws);
       int s = w[i];
       for (int p = 1; p < parts; ++p) s += w[(size_t)p * mn + i];
-      static_cast<int*>(C)[i] = s + bias_i(a, col);
+      if (a.row_scale) static_cast<_Float16*>(C)[i] = dq_out(a, (int)(i / (size_t)a.N), col, s);
+      else static_cast<int*>(C)[i] = s + bias_i(a, col);
     }
   }
 }
@@ -65,10 +66,10 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const RunArgs& a, int out_f16, hipStream_t st) {
+hipError_t launch_finalize(const RunArgs& a, int acc_fp, hipStream_t st) {
   const size_t mn = (size_t)a.M * a.N;
   const int parts = a.out_mode == OUT_PARTIAL ? a.k_parts : 1;
-  if (out_f16)
+  if (acc_fp)
     hipLaunchKernelGGL(finalize_kernel<true>, dim3(grid_for(mn, 256)), dim3(256), 0, st, a.ws, a.C, mn, parts, a);
   else
     hipLaunchKernelGGL(finalize_kernel<false>, dim3(grid_for(mn, 256)), dim3(256), 0, st, a.ws, a.C, mn, parts, a);

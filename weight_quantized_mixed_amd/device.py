@@ -39,14 +39,33 @@ def host_to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
+def quantize_rows(A, Q=None, scales=None, stream=None):
+    """Per-row symmetric int8 codes and fp32 scales of fp16 A [M, K] (one kernel)."""
+    M, K = A.shape
+    if Q is None:
+        Q = torch.empty((M, K), dtype=torch.int8, device=A.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=A.device)
+    _q.qgemm_quantize_rows(_ptr(A), M, K, _ptr(Q), _ptr(scales), _stream(stream))
+    return Q, scales
+
+
 class QGemm:
-    """One plan: C[M,N] = A[M,K] . dequant(W) for a fixed shape and format."""
+    """One plan: C[M,N] = A[M,K] . dequant(W) for a fixed shape and format.
+
+    dequant_output: int8 activations with an fp16 output dequantised by per-row
+    and per-column scales (run_scaled) instead of the int32 accumulator.
+    """
 
     def __init__(self, M, N, K, w_dtype, group_size=0, has_zeros=False, k_parts=1,
-                 deterministic=False, device="cuda"):
+                 deterministic=False, device="cuda", dequant_output=False):
         self.M, self.N, self.K, self.w_dtype = int(M), int(N), int(K), w_dtype
         self.a_dtype = A_DTYPE[w_dtype]
         self.out_dtype, self.accum_dtype = OUT_DTYPE[self.a_dtype]
+        if dequant_output:
+            if self.a_dtype != "i8":
+                raise ValueError("dequant_output is for int8 activations")
+            self.out_dtype = "f16"
         self.device = torch.device(device)
         flags = _q.QGEMM_DETERMINISTIC if deterministic else 0
         self.plan, self.packed_bytes, self.ws_bytes = _q.qgemm_create(
@@ -89,4 +108,15 @@ class QGemm:
         else:
             _q.qgemm_run_ex(self.plan, self.M if M is None else M, _ptr(A), _ptr(packed), _ptr(bias),
                             _ptr(C), _ptr(ws), wsb, _stream(stream))
+        return C
+
+    def run_scaled(self, A, packed, row_scales, col_scales, bias=None, C=None, ws=None, stream=None, M=None):
+        """fp16 C = acc . row_scales[m] . col_scales[n] (+ bias) for int8 A (dequant_output plans)."""
+        if C is None:
+            C = self.new_output(M)
+        if ws is None:
+            ws = self.workspace()
+        _q.qgemm_run_scaled(self.plan, self.M if M is None else M, _ptr(A), _ptr(packed), _ptr(row_scales),
+                            _ptr(col_scales), _ptr(bias), _ptr(C), _ptr(ws),
+                            0 if ws is None else ws.numel(), _stream(stream))
         return C

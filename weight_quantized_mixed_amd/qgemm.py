@@ -21,8 +21,8 @@ QGEMM_OK, QGEMM_ERR_INVALID_ARG, QGEMM_ERR_UNSUPPORTED, QGEMM_ERR_NO_MEMORY, QGE
 QGEMM_DETERMINISTIC = 1
 QGEMM_PATH_GEMV, QGEMM_PATH_MFMA = 1, 2
 
-EXPORTED = ("qgemm_create", "qgemm_pack_weights", "qgemm_run", "qgemm_run_ex", "qgemm_destroy",
-            "qgemm_plan_path", "qgemm_status_string")
+EXPORTED = ("qgemm_create", "qgemm_pack_weights", "qgemm_run", "qgemm_run_ex", "qgemm_run_scaled",
+            "qgemm_quantize_rows", "qgemm_destroy", "qgemm_plan_path", "qgemm_status_string")
 
 
 class QGemmError(RuntimeError):
@@ -62,6 +62,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qgemm_run.restype = c_i32
     lib.qgemm_run_ex.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
     lib.qgemm_run_ex.restype = c_i32
+    lib.qgemm_run_scaled.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
+    lib.qgemm_run_scaled.restype = c_i32
+    lib.qgemm_quantize_rows.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_p]
+    lib.qgemm_quantize_rows.restype = c_i32
     lib.qgemm_destroy.argtypes = [c_p]
     lib.qgemm_destroy.restype = None
     lib.qgemm_plan_path.argtypes = [c_p]
@@ -109,6 +113,21 @@ def qgemm_run_ex(plan, M, A, packed, bias, C, workspace, workspace_bytes, stream
                              workspace or None, int(workspace_bytes), stream or None)
     if st != QGEMM_OK:
         raise QGemmError(st, "qgemm_run_ex")
+
+
+def qgemm_run_scaled(plan, M, A, packed, row_scales, col_scales, bias, C, workspace, workspace_bytes,
+                     stream=0):
+    st = load().qgemm_run_scaled(plan, int(M), A or None, packed or None, row_scales or None,
+                                 col_scales or None, bias or None, C or None, workspace or None,
+                                 int(workspace_bytes), stream or None)
+    if st != QGEMM_OK:
+        raise QGemmError(st, "qgemm_run_scaled")
+
+
+def qgemm_quantize_rows(A, M, K, Q, scales, stream=0):
+    st = load().qgemm_quantize_rows(A or None, int(M), int(K), Q or None, scales or None, stream or None)
+    if st != QGEMM_OK:
+        raise QGemmError(st, "qgemm_quantize_rows")
 
 
 def qgemm_destroy(plan):
