@@ -34,15 +34,19 @@ MALL_BYTES = 256 << 20
 METRIC = "qgemm µs + TFLOPS/TOPS + HBM GB/s vs roofline, M=1..16384, N=K=16384"
 
 
-def alg_bytes(M, N, K, w_dtype, g, zeros):
-    """Bytes the computation must move at least once: packed W, scales, zeros, A, C."""
+def alg_bytes(M, N, K, w_dtype, g, zeros, bias=False, dq=False):
+    """Bytes the computation must move at least once: packed W, scales, zeros, A, C
+    (+ bias; + per-row and per-column scales of a dequantised int8 output)."""
     G = 0 if g == 0 else (1 if g < 0 else K // g)
     a_sz = 2 if w_dtype in ("i4", "u4", "f16") else 1
-    c_sz = 2 if a_sz == 2 else 4
-    return (N * K * BITS[w_dtype]) // 8 + N * G * 2 * (2 if zeros else 1) + M * K * a_sz + M * N * c_sz
+    c_sz = 2 if (a_sz == 2 or dq) else 4
+    extra = (N * c_sz if bias else 0) + ((M + N) * 4 if dq else 0)
+    return (N * K * BITS[w_dtype]) // 8 + N * G * 2 * (2 if zeros else 1) + M * K * a_sz + M * N * c_sz + extra
 
 
 def label(c):
+    if c["w"] == "quant":
+        return f"quantize_rows M={c['M']} K={c['K']}"
     s = f"{c['w']} M={c['M']} N={c['N']} K={c['K']}"
     if c["w"] in ("i4", "u4"):
         s += f" g={c.get('g', 0)}"
@@ -50,6 +54,10 @@ def label(c):
         s += " zeros"
     if c.get("kp", 1) > 1:
         s += f" kp={c['kp']}"
+    if c.get("dq"):
+        s += " dequant-fp16"
+    if c.get("bias"):
+        s += " bias"
     return s
 
 
@@ -84,23 +92,35 @@ class Bench:
         g, z, kp = c.get("g", 0), c.get("zeros", False), c.get("kp", 1)
         if wd not in ("i4", "u4"):
             g = 0
-        self.q = QGemm(M, N, K, wd, g, z, kp)
+        self.dq, bias = bool(c.get("dq")), bool(c.get("bias"))
+        self.q = QGemm(M, N, K, wd, g, z, kp, dequant_output=self.dq)
         self.packed = _weights(c, self.q, seed)
         A = host_to_device(synth.draw_activations(M, K, self.q.a_dtype, seed + M))
         n_a = 1 if A.numel() * A.element_size() >= 2 * MALL_BYTES else len(self.packed)
         self.As = [A] + [A.clone() for _ in range(n_a - 1)]
         self.C = self.q.new_output()
         self.ws = self.q.workspace()
+        self.bias = host_to_device(synth.draw_bias(N, self.q.out_dtype, seed + 5)) if bias else None
+        if self.dq:
+            self.rs = host_to_device(synth.draw_col_scales(M, seed + 6))
+            self.cs = host_to_device(synth.draw_col_scales(N, seed + 7))
         self.i = 0
-        self.bytes = alg_bytes(M, N, K, wd, g, z)
+        self.bytes = alg_bytes(M, N, K, wd, g, z, bias, self.dq)
         self.flops = 2.0 * M * N * K
         self.a_kind = "f16" if wd in ("i4", "u4", "f16") else "i8"
+        self.path_name = "gemv" if self.q.path == 1 else "mfma"
         torch.cuda.synchronize()
 
     def call(self):
         j = self.i
         self.i += 1
-        self.q.run(self.As[j % len(self.As)], self.packed[j % len(self.packed)], self.C, self.ws)
+        A, W = self.As[j % len(self.As)], self.packed[j % len(self.packed)]
+        if self.dq:
+            self.q.run_scaled(A, W, self.rs, self.cs, self.bias, self.C, self.ws)
+        elif self.bias is not None:
+            self.q.run(A, W, self.C, self.ws, bias=self.bias)
+        else:
+            self.q.run(A, W, self.C, self.ws)
 
     def timed(self, n):
         """Seconds per call over n back-to-back calls (HIP events on the launch stream)."""
@@ -150,6 +170,38 @@ class Bench:
         self.q.close()
 
 
+class QuantBench(Bench):
+    """qgemm_quantize_rows on fp16 [M, K] activations: reads 2 bytes and writes 1 byte
+    per element plus one fp32 scale per row (HBM-bound)."""
+
+    def __init__(self, c, seed):
+        import torch
+        import synth
+        from weight_quantized_mixed_amd.device import host_to_device
+        self.c = c
+        M, K = c["M"], c["K"]
+        A = host_to_device(synth.draw_fp16_activations(M, K, seed))
+        n = 1 if A.numel() * 2 >= 2 * MALL_BYTES else min(64, -(-(4 * MALL_BYTES) // (A.numel() * 2)))
+        self.packed = [A] + [A.clone() for _ in range(n - 1)]   # the input ring
+        self.Q = torch.empty((M, K), dtype=torch.int8, device=A.device)
+        self.S = torch.empty(M, dtype=torch.float32, device=A.device)
+        self.i = 0
+        self.bytes = M * K * 3 + M * 4
+        self.flops = 0.0
+        self.a_kind = "f16"
+        self.path_name = "quant"
+        torch.cuda.synchronize()
+
+    def call(self):
+        from weight_quantized_mixed_amd.device import quantize_rows
+        j = self.i
+        self.i += 1
+        quantize_rows(self.packed[j % len(self.packed)], self.Q, self.S)
+
+    def close(self):
+        pass
+
+
 def measure_grid_entry(b, bursts=50):
     """Median (p10, p90) over bursts of back-to-back calls replayed from one HIP graph,
     so that small calls are timed on the GPU rather than at the host's launch rate."""
@@ -169,7 +221,7 @@ def measure_grid_entry(b, bursts=50):
             "p90_us": round(samples[min(len(samples) - 1, (9 * len(samples)) // 10)] * 1e6, 3),
             ("TFLOPS" if b.a_kind == "f16" else "TOPS"): round(b.flops / t / 1e12, 3),
             "GBps": round(b.bytes / t / 1e9, 1), "bound": bound, "roofline_frac": round(frac, 4),
-            "path": "gemv" if b.q.path == 1 else "mfma"}
+            "path": b.path_name}
 
 
 GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128, 512)]
@@ -181,8 +233,18 @@ GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128
            for (K, N) in ((4096, 11008), (11008, 4096), (4096, 4096), (4096, 32000)) for kp in (1, 4)]
         + [{"w": "i4", "M": 1, "N": 4096, "K": 4096, "g": 128}]
         + [{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": g} for g in (0, -1) for M in (1, 32, 128, 512)]
+        # bias epilogue; int8 products with the dequantised fp16 output; the per-row
+        # int8 quantiser of fp16 activations
+        + [{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128, "bias": True} for M in (1, 512)]
+        + [{"w": w, "M": M, "N": 16384, "K": 16384, "dq": True, "bias": True} for w in ("i8", "i2")
+           for M in (1, 512)]
+        + [{"w": "quant", "M": M, "K": 16384} for M in (512, 16384)]
         + [{"w": "f16", "M": 16384, "N": 16384, "K": 16384},
            {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}])
+
+
+def make_bench(c, seed):
+    return QuantBench(c, seed) if c["w"] == "quant" else Bench(c, seed)
 
 
 HEADLINE_PROFILE = os.path.join(ROOT, "profiles", "gemv_w4a16_m1_n16384_k16384.md")
@@ -296,7 +358,7 @@ def main():
         for i, c in enumerate(GRID):
             if args.only and args.only not in label(c):
                 continue
-            b = Bench(c, synth.seed_for(6, i))
+            b = make_bench(c, synth.seed_for(6, i))
             grid.append(measure_grid_entry(b))
             print(f"[bench] {grid[-1]}", file=sys.stderr, flush=True)
             b.close()

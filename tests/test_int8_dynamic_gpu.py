@@ -30,7 +30,7 @@ def _edge_rows(A):
     return A
 
 
-@pytest.mark.parametrize("M,K", [(1, 16384), (7, 4096), (300, 1024), (2, 8), (5, 72)])
+@pytest.mark.parametrize("M,K", [(1, 16384), (7, 4096), (300, 1024), (2, 8), (5, 72), (3, 32768), (2, 40960)])
 def test_quantize_rows_bit_exact(M, K):
     say(f"case quantize M={M} K={K}")
     A = _edge_rows(synth.draw_fp16_activations(M, K, seed=M + K))
