@@ -44,7 +44,7 @@ def test_w4a16_llama_shapes(M, K, N, kp):
     _check_sampled(c, rows, cols, f"W4A16 {M}x{K}x{N} kp={kp}")
 
 
-@pytest.mark.parametrize("M", [1, 32, 128, 512])
+@pytest.mark.parametrize("M", [1, 8, 32, 128, 512])
 @pytest.mark.parametrize("w_dtype,kp", [("i8", 1), ("i8", 4), ("i2", 1), ("i2", 4)])
 def test_int_grid_full(M, w_dtype, kp):
     say(f"{w_dtype} M={M} N=K=16384 kp={kp}")

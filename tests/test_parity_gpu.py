@@ -48,6 +48,11 @@ SMALL = [
     (70, 136, 1920, "i4", 96, False),
     (40, 264, 1536, "u4", 384, True),
     (300, 520, 1536, "i4", 384, False),
+    # int8 / int2 rows 2..8 on the matrix cores (ragged last 64-column block)
+    (2, 200, 1024, "i8", 0, False),
+    (3, 72, 2048, "i2", 0, False),
+    (8, 264, 2048, "i2", 0, False),
+    (6, 1000, 512, "i8", 0, False),
     # M = 1 with 16-column workgroups at k_parts 1, 64-column blocks at k_parts 3
     (1, 2752, 512, "u4", 128, True),
     (1, 2752, 1024, "i2", 0, False),

@@ -17,6 +17,7 @@ struct qg_choice {
   int tile;          // LDS-staged MFMA tile (used when dl_tile < 0)
   int gemv_waves;    // GEMV waves per workgroup
   bool gemv_narrow;  // M = 1 with fewer than 128 blocks of 64 columns: 16-column workgroups
+  bool gemv_mfma;    // int8 / int2 GEMV on the matrix cores
 };
 
 struct qgemm_plan {
@@ -63,6 +64,18 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
   L->total = L->s_offset + L->s_bytes;
   return QGEMM_OK;
 }
+
+// formats (bit per format) whose GEMV runs on the matrix cores (int8, int2 only),
+// from this many rows on: the matrix cores take up to 16 rows for the price of
+// one (W2A8 M = 8: 13.9 us against 31.5 us with dot products), while at M = 1 the
+// dot-product GEMV reads its activations through the scalar unit and stays
+// ahead (12.6 against 13.2 us)
+#ifndef QG_GEMV_MFMA_FMTS
+#define QG_GEMV_MFMA_FMTS ((1 << FMT_I8) | (1 << FMT_I2))
+#endif
+#ifndef QG_GEMV_MFMA_MIN_M
+#define QG_GEMV_MFMA_MIN_M 2
+#endif
 
 #ifndef QG_GEMV_TARGET_WAVES
 #define QG_GEMV_TARGET_WAVES 2048
@@ -119,6 +132,8 @@ qg_choice choose(const qgemm_plan* p, int64_t M) {
                                                           scale_mode(p->L.fmt, p->group_size))
                                         : -1;
   c.gemv_narrow = c.path == QGEMM_PATH_GEMV && choose_gemv_narrow(p, M);
+  c.gemv_mfma = c.path == QGEMM_PATH_GEMV && !c.gemv_narrow && M >= QG_GEMV_MFMA_MIN_M &&
+                ((QG_GEMV_MFMA_FMTS >> p->L.fmt) & 1);
   c.gemv_waves = choose_gemv_waves(p, c.gemv_narrow);
   return c;
 }
@@ -190,7 +205,8 @@ qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const vo
                 : launch_fill_zero(C, (size_t)M * plan->N * 4, st);
   if (e == hipSuccess)
     e = ch.path == QGEMM_PATH_GEMV ? (ch.gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
-                                                     : launch_gemv(plan->L.fmt, a, st))
+                                      : ch.gemv_mfma  ? launch_gemv_mfma(plan->L.fmt, a, st)
+                                                      : launch_gemv(plan->L.fmt, a, st))
         : ch.dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, ch.dl_tile, a, st)
         : launch_mfma(plan->L.fmt, ch.tile, a, st);
   if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))

@@ -1,0 +1,209 @@
+// Skinny-M int8 / int2 path on the matrix cores (M <= 8).
+//
+// The packed blob already holds every 16-column superblock in the lane order of
+// a gfx950 16x16 MFMA B operand (lane l: column l % 16, K group l / 16), so one
+// wave-wide 16-byte load of a superblock is an MFMA operand as it stands
+// (int8), or four of them after masking (int2): no LDS, no transposition.  A
+// workgroup owns 64 columns (four superblock columns) and a k-part; its waves
+// take the part's superblock rows in turn (as the VALU GEMV does) and meet in
+// LDS at the end.  The activation rows ride in the A operand: lane l loads the
+// K group l / 16 of row l % 16 (rows past M repeat row M - 1, and their results
+// are dropped), so up to 16 rows cost the same instructions as one.
+//
+// int8: one v_mfma_i32_16x16x64_i8 per superblock and column block.
+// int2: word t of piece g holds positions 64 g + 16 t + 4 j + b (class j, byte b);
+// masking word t with 0x03, 0x0C, 0x30 or 0xC0 per byte keeps class j as the byte
+// value 4^j c (the top class two's complement, so 64 q as a signed byte), and the
+// four masked words of a piece are the B operand of class j.  The matching A
+// operand is dword 4 t + j of the lane's 64-byte activation slice, a choice of
+// registers.  Classes 0-2 are offset-binary (c = q + 2): one more MFMA per class
+// against a B of ones gives the activation sums that the correction subtracts.
+// Per word this is four VALU masks, where the dot-product GEMV needs four masks
+// and four dot products.
+#include "qgemm_internal.hpp"
+
+namespace qg {
+namespace {
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ int4v as_i4(const uint4& v) { return int4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
+
+// one 16-byte load as a vector (kept whole)
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u t = *reinterpret_cast<const v4u*>(p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// a register copy the compiler cannot fold into a vector shuffle (which it lowers
+// through scratch memory when building the transposed activation operands)
+__device__ __forceinline__ int mv(uint32_t x) {
+  int r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+__device__ __forceinline__ int4v masked(const uint4& w, uint32_t m) {
+  return int4v{(int)(w.x & m), (int)(w.y & m), (int)(w.z & m), (int)(w.w & m)};
+}
+
+__device__ __forceinline__ int4v mfma(const int4v& A, const int4v& B, const int4v& C) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, C, 0, 0, 0);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs a) {
+  constexpr bool I2 = FMT == FMT_I2;
+  constexpr int KB = kb_of(FMT);   // positions per superblock: 256 (int2), 64 (int8)
+  constexpr int AV = KB / 64;      // 16-byte activation vectors per lane and superblock
+  constexpr int NC = I2 ? 4 : 1;   // MFMAs per column block and superblock (int2 classes)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = blockIdx.x, part = blockIdx.y;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  const int u0 = (int)((int64_t)part * a.n_units / a.k_parts);
+  const int u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
+  const int kb0 = u0 * a.unit_kb, kb1 = u1 * a.unit_kb;
+  // superblock rows of this wave, in turn with the other waves (wave-uniform)
+  const int cnt = __builtin_amdgcn_readfirstlane(kb1 - kb0 > wave ? (kb1 - kb0 - wave + a.waves - 1) / a.waves : 0);
+  auto row_of = [&](int j) { return __builtin_amdgcn_readfirstlane(kb0 + wave + j * a.waves); };
+
+  const uint4* __restrict__ Wl = a.W + (size_t)rb * 4 * 64 + lane;  // column block rb*4 + cb at + cb*64
+  const uint32_t sb_stride = (uint32_t)a.NB * 64u;                   // uint4 per superblock row
+  // this lane's activation slice: row r16, K group g of each superblock.  Lanes of
+  // rows past M read row M - 1 (results dropped): the loads stay unconditional,
+  // since masking them off makes the compiler drain every load in flight at the
+  // end of the masked block.
+  const uint4* __restrict__ Al =
+      reinterpret_cast<const uint4*>(static_cast<const int8_t*>(a.A) + (size_t)min(r16, a.M - 1) * a.K) + g * AV;
+
+  // A is loaded before the weights, so that waiting for a stage's activations
+  // never waits for the weight loads of the stage after it
+  struct Stage {
+    uint4 av[AV];
+    uint4 w[4];
+  };
+  auto load = [&](Stage& s, int j) {
+    const uint32_t kb = (uint32_t)row_of(min(j, cnt - 1));
+#pragma unroll
+    for (int i = 0; i < AV; ++i) s.av[i] = load16(Al + kb * (KB / 16) + i);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) s.w[cb] = stream_load(Wl + kb * sb_stride + cb * 64);
+  };
+
+  int4v acc[4][NC];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[cb][c] = int4v{0, 0, 0, 0};
+  int4v accS = int4v{0, 0, 0, 0};  // int2: activation sums of classes 0-2
+
+  auto consume = [&](const Stage& s) {
+    if constexpr (I2) {
+      // the A operand of class j takes dword 4 t + j of the lane's 64-byte slice as
+      // its dword t
+      int4v A[4];
+      A[0] = int4v{mv(s.av[0].x), mv(s.av[1].x), mv(s.av[2].x), mv(s.av[3].x)};
+      A[1] = int4v{mv(s.av[0].y), mv(s.av[1].y), mv(s.av[2].y), mv(s.av[3].y)};
+      A[2] = int4v{mv(s.av[0].z), mv(s.av[1].z), mv(s.av[2].z), mv(s.av[3].z)};
+      A[3] = int4v{mv(s.av[0].w), mv(s.av[1].w), mv(s.av[2].w), mv(s.av[3].w)};
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint4 w = s.w[cb];
+        acc[cb][0] = mfma(A[0], masked(w, 0x03030303u), acc[cb][0]);
+        acc[cb][1] = mfma(A[1], masked(w, 0x0C0C0C0Cu), acc[cb][1]);
+        acc[cb][2] = mfma(A[2], masked(w, 0x30303030u), acc[cb][2]);
+        acc[cb][3] = mfma(A[3], masked(w, 0xC0C0C0C0u), acc[cb][3]);
+      }
+      const int4v ones = int4v{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+      accS = mfma(A[0], ones, accS);
+      accS = mfma(A[1], ones, accS);
+      accS = mfma(A[2], ones, accS);
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[cb][0] = mfma(as_i4(s.av[0]), as_i4(s.w[cb]), acc[cb][0]);
+    }
+  };
+
+  // two register stages; the steady loop never loads past the wave's rows.  The
+  // fences keep each stage's loads ahead of the other stage's MFMAs, so that the
+  // wait for one stage never covers the loads of the next.
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  Stage s0, s1;
+  if (cnt > 0) {
+    int j = 0;
+    load(s0, 0);
+    for (; j + 2 < cnt; j += 2) {
+      fence();
+      load(s1, j + 1);
+      fence();
+      consume(s0);
+      fence();
+      load(s0, j + 2);
+      fence();
+      consume(s1);
+    }
+    fence();
+    if (j + 1 < cnt) {
+      load(s1, j + 1);
+      fence();
+      consume(s0);
+      fence();
+      consume(s1);
+    } else {
+      consume(s0);
+    }
+  }
+
+  // lane l holds rows 4 (l / 16) + r of column l % 16 of each column block; the
+  // waves meet in LDS
+  __shared__ int red[GEMV_MAX_WAVES][4][4][64];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int v = acc[cb][0][r];
+      if constexpr (I2)  // classes 0..2 are offset-binary (q + 2)
+        v += (acc[cb][1][r] >> 2) + (acc[cb][2][r] >> 4) + (acc[cb][3][r] >> 6) - 2 * accS[r];
+      red[wave][cb][r][lane] = v;
+    }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 4 * 4 * 64; idx += blockDim.x) {
+    const int cb = idx >> 8, r = (idx >> 6) & 3, ln = idx & 63;
+    const int row = 4 * (ln >> 4) + r, col = rb * 64 + cb * 16 + (ln & 15);
+    if (row >= a.M || col >= a.N) continue;
+    int s = 0;
+    for (int w = 0; w < a.waves; ++w) s += red[w][cb][r][ln];
+    const size_t o = (size_t)row * a.N + col;
+    if (a.out_mode == OUT_STORE) {
+      if (a.row_scale) static_cast<_Float16*>(a.C)[o] = dq_out(a, row, col, s);
+      else static_cast<int*>(a.C)[o] = s + bias_i(a, col);
+    } else if (a.out_mode == OUT_ATOMIC) {
+      atomicAdd(int_atomic_target(a) + o, s);
+    } else {
+      static_cast<int*>(a.ws)[(size_t)part * a.M * a.N + o] = s;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_mfma(int fmt, const RunArgs& a, hipStream_t st) {
+  if (a.M < 1 || a.M > 16) return hipErrorInvalidValue;
+  const dim3 grid((a.N + 63) / 64, a.k_parts), block(64 * a.waves);
+  if (fmt == FMT_I8) hipLaunchKernelGGL(gemv_mfma_kernel<FMT_I8>, grid, block, 0, st, a);
+  else if (fmt == FMT_I2) hipLaunchKernelGGL(gemv_mfma_kernel<FMT_I2>, grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace qg

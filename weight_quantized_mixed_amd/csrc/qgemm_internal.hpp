@@ -113,6 +113,8 @@ hipError_t launch_pack(const Layout& L, const void* w, const void* s, const void
 hipError_t launch_gemv(int fmt, const RunArgs& a, hipStream_t st);
 // M = 1 with 16-column workgroups (gemv16.hip), for matrices with few 64-column blocks
 hipError_t launch_gemv16(int fmt, const RunArgs& a, hipStream_t st);
+// int8 / int2 skinny-M on the matrix cores, B operands straight from the blob (gemv_mfma.hip)
+hipError_t launch_gemv_mfma(int fmt, const RunArgs& a, hipStream_t st);
 hipError_t launch_mfma(int fmt, int tile, const RunArgs& a, hipStream_t st);
 // direct-load ring kernel (mfma_dl.hip): the tile for a problem, or -1 when the
 // problem needs the LDS-staged kernel (int4 with per-piece scale groups)
