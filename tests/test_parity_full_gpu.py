@@ -32,7 +32,8 @@ def _check_sampled(c, rows, cols, what):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (1, 4096, 11008), (1, 11008, 4096),
-                                   (1, 4096, 32000), (128, 4096, 11008), (128, 11008, 4096),
+                                   (1, 4096, 32000), (8, 4096, 11008), (32, 11008, 4096),
+                                   (128, 4096, 11008), (128, 11008, 4096),
                                    (128, 4096, 4096), (128, 4096, 32000)])
 @pytest.mark.parametrize("kp", [1, 4])
 def test_w4a16_llama_shapes(M, K, N, kp):

@@ -48,6 +48,13 @@ SMALL = [
     (70, 136, 1920, "i4", 96, False),
     (40, 264, 1536, "u4", 384, True),
     (300, 520, 1536, "i4", 384, False),
+    # int4 / uint4 rows 5..32 on the matrix cores (bias-folded operands, per-superblock fold)
+    (5, 200, 1024, "i4", 128, False),
+    (16, 264, 1024, "u4", 128, True),
+    (17, 300, 2048, "i4", -1, False),
+    (32, 520, 1024, "u4", 128, True),
+    (12, 136, 512, "i4", 0, False),
+    (24, 72, 1536, "u4", 384, True),
     # int8 / int2 rows 2..8 on the matrix cores (ragged last 64-column block)
     (2, 200, 1024, "i8", 0, False),
     (3, 72, 2048, "i2", 0, False),

@@ -18,6 +18,7 @@ struct qg_choice {
   int gemv_waves;    // GEMV waves per workgroup
   bool gemv_narrow;  // M = 1 with fewer than 128 blocks of 64 columns: 16-column workgroups
   bool gemv_mfma;    // int8 / int2 GEMV on the matrix cores
+  bool gemv_mfma4;   // int4 / uint4 GEMV on the matrix cores (also for 8 < M <= 32)
 };
 
 struct qgemm_plan {
@@ -75,6 +76,20 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
 #endif
 #ifndef QG_GEMV_MFMA_MIN_M
 #define QG_GEMV_MFMA_MIN_M 2
+#endif
+// rows for which int4 / uint4 (groups of whole superblocks) take the matrix-core
+// GEMV instead of the dot-product GEMV (M <= 8) or the direct-load kernel.
+// Measured at N = K = 16384, g = 128: M = 2 / 4 / 8 / 16 / 32 ran 40.8 / 42.1 /
+// 44.3 / 48.1 / 63.4 us against 29.8 / 41.3 / 64.5 / 67.8 / 69.7 us; unscaled
+// (g = 0) the direct-load kernel keeps M = 32 (58.9 against 63.4 us).
+#ifndef QG_GEMV4_MFMA_MIN_M
+#define QG_GEMV4_MFMA_MIN_M 5
+#endif
+#ifndef QG_GEMV4_MFMA_MAX_M
+#define QG_GEMV4_MFMA_MAX_M 32
+#endif
+#ifndef QG_GEMV4_MFMA_MAX_M_UNSCALED
+#define QG_GEMV4_MFMA_MAX_M_UNSCALED 16
 #endif
 
 #ifndef QG_GEMV_TARGET_WAVES
@@ -134,6 +149,10 @@ qg_choice choose(const qgemm_plan* p, int64_t M) {
   c.gemv_narrow = c.path == QGEMM_PATH_GEMV && choose_gemv_narrow(p, M);
   c.gemv_mfma = c.path == QGEMM_PATH_GEMV && !c.gemv_narrow && M >= QG_GEMV_MFMA_MIN_M &&
                 ((QG_GEMV_MFMA_FMTS >> p->L.fmt) & 1);
+  const int smode = scale_mode(p->L.fmt, p->group_size);
+  c.gemv_mfma4 = (p->L.fmt == FMT_I4 || p->L.fmt == FMT_U4) && !c.gemv_narrow && smode != SC_PIECE &&
+                 M >= QG_GEMV4_MFMA_MIN_M &&
+                 M <= (smode == SC_NONE ? QG_GEMV4_MFMA_MAX_M_UNSCALED : QG_GEMV4_MFMA_MAX_M);
   c.gemv_waves = choose_gemv_waves(p, c.gemv_narrow);
   return c;
 }
@@ -204,7 +223,8 @@ qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const vo
         : bias  ? launch_fill_bias(a, st)
                 : launch_fill_zero(C, (size_t)M * plan->N * 4, st);
   if (e == hipSuccess)
-    e = ch.path == QGEMM_PATH_GEMV ? (ch.gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
+    e = ch.gemv_mfma4 ? launch_gemv_mfma4(plan->L.fmt, a, st)
+        : ch.path == QGEMM_PATH_GEMV ? (ch.gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
                                       : ch.gemv_mfma  ? launch_gemv_mfma(plan->L.fmt, a, st)
                                                       : launch_gemv(plan->L.fmt, a, st))
         : ch.dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, ch.dl_tile, a, st)

@@ -43,12 +43,10 @@ __device__ __forceinline__ uint4 load16(const uint4* p) {
 }
 
 // a register copy the compiler cannot fold into a vector shuffle (which it lowers
-// through scratch memory when building the transposed activation operands)
-__device__ __forceinline__ int mv(uint32_t x) {
-  int r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
+// through scratch memory when building the transposed activation operands): an
+// identity DPP move, which unlike inline assembly stays visible to the pass that
+// inserts the wait states between a VALU write and the MFMA that reads it
+__device__ __forceinline__ int mv(uint32_t x) { return __builtin_amdgcn_mov_dpp((int)x, 0xE4, 0xF, 0xF, false); }
 
 __device__ __forceinline__ int4v masked(const uint4& w, uint32_t m) {
   return int4v{(int)(w.x & m), (int)(w.y & m), (int)(w.z & m), (int)(w.w & m)};

@@ -1,0 +1,212 @@
+// Skinny-M int4 / uint4 path on the matrix cores (2 <= M <= 32).
+//
+// Lane l of a wave works on column l % 16 of a 16-column superblock and K group
+// g = l / 16 of every 32-position MFMA step.  In the packed blob, word g of the
+// piece of step s holds exactly that group's eight positions (nibble slots 0..7 =
+// positions 0,2,4,6,1,3,5,7), so the B operand of step s is four dword loads (one
+// per step, 256 contiguous bytes per wave) and four v_and_or_b32: slot pair
+// (jj, jj + 4) becomes the fp16 pair 1024 + q, with no subtraction (the bias
+// folding of the dot-product GEMV).  The A operand is a row of activations
+// (lane l: row l % 16 of the row block, positions 32 s + 8 g .. + 7), so one set
+// of B operands serves up to 16 rows per MFMA, two row blocks up to 32.
+//
+// Per superblock and column block the MFMAs accumulate T = sum a (1024 + b + q),
+// with b the offset of the code (8 for signed int4, 0 for uint4), into a
+// temporary; three more MFMAs per superblock against a B of fp16 ones give the
+// row sums S = sum a, and the superblock is folded into the result as
+//   acc += s * (T - (1024 + b + z) * S)                    (all in fp32)
+// which is sum a (q - z) s for its scale group (z = 0 without zero points, s = 1
+// without scales).  Products a (1024 + q) are exact in fp32 and a superblock sums
+// only 128 of them, so the fold loses no more than fp32 rounding of T.
+// Groups of whole superblocks (or one group over K) only; 32- and 64-position
+// groups take the dot-product GEMV.
+#include "qgemm_internal.hpp"
+
+namespace qg {
+namespace {
+
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// (x & m) | c, left to the compiler (v_and_or_b32): its results feed an MFMA a few
+// instructions later, and the compiler inserts the wait states that a VALU write
+// followed by a matrix-core read of the same register needs, which it cannot do
+// for an inline-assembly writer
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
+
+__device__ __forceinline__ uint32_t stream_load32(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u t = *reinterpret_cast<const v4u*>(p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ float4v mfma(const uint4& A, const uint4& B, const float4v& C) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8v, A), __builtin_bit_cast(half8v, B), C, 0, 0, 0);
+}
+
+// VAR: 0 unscaled, 1 scaled, 2 scaled with zero points
+template <int FMT, int MB, int VAR>
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs a) {
+  constexpr int KB = 128, NS = 4;  // positions and 32-position MFMA steps per superblock
+  constexpr bool SCALED = VAR >= 1, ZEROS = VAR == 2;
+  constexpr float BIAS = FMT == FMT_I4 ? 1032.f : 1024.f;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = blockIdx.x, part = blockIdx.y;
+  const int g = lane >> 4, n16 = lane & 15;
+
+  const int u0 = (int)((int64_t)part * a.n_units / a.k_parts);
+  const int u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
+  const int kb0 = u0 * a.unit_kb, kb1 = u1 * a.unit_kb;
+  const int cnt = __builtin_amdgcn_readfirstlane(kb1 - kb0 > wave ? (kb1 - kb0 - wave + a.waves - 1) / a.waves : 0);
+  auto row_of = [&](int j) { return __builtin_amdgcn_readfirstlane(kb0 + wave + j * a.waves); };
+
+  // word g of piece (s, n16) of superblock (kb, column block rb*4 + cb)
+  const uint32_t* __restrict__ Wd = reinterpret_cast<const uint32_t*>(a.W) + ((size_t)rb * 4 * 64 + n16) * 4 + g;
+  const uint32_t sb_stride = (uint32_t)a.NB * 256u;  // dwords per superblock row
+  // activation rows of the lane (rows past M repeat row M - 1; results dropped)
+  const uint4* __restrict__ Al[MB];
+#pragma unroll
+  for (int r = 0; r < MB; ++r)
+    Al[r] = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.A) + (size_t)min(r * 16 + n16, a.M - 1) * a.K) + g;
+
+  struct Stage {
+    uint4 av[MB][NS];  // A operand of each row block and step
+    uint32_t w[4][NS];  // packed word of each column block and step
+    uint32_t sc[4];     // raw scale (| zero << 16) of each column block
+  };
+  auto load = [&](Stage& s, int j) {
+    const uint32_t kb = (uint32_t)row_of(min(j, cnt - 1));
+#pragma unroll
+    for (int r = 0; r < MB; ++r)
+#pragma unroll
+      for (int t = 0; t < NS; ++t) s.av[r][t] = load16(Al[r] + kb * (KB / 8) + t * 4);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int t = 0; t < NS; ++t) s.w[cb][t] = stream_load32(Wd + kb * sb_stride + cb * 256 + t * 64);
+    if constexpr (SCALED) {
+      const uint32_t grp = a.sb_per_group == 1 ? kb : kb / (uint32_t)a.sb_per_group;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint32_t col = (uint32_t)(rb * 64 + cb * 16 + n16);
+        if constexpr (ZEROS) s.sc[cb] = static_cast<const uint32_t*>(a.S)[grp * (uint32_t)a.Npad + col];
+        else s.sc[cb] = static_cast<const uint16_t*>(a.S)[grp * (uint32_t)a.Npad + col];
+      }
+    }
+  };
+
+  float4v acc[MB][4];
+#pragma unroll
+  for (int r = 0; r < MB; ++r)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[r][cb] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  const uint4 ONES = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  auto consume = [&](const Stage& s) {
+    float4v T[MB][4], S[MB];
+#pragma unroll
+    for (int r = 0; r < MB; ++r) {
+      S[r] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) T[r][cb] = float4v{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint32_t w = s.w[cb][t];
+        const uint4 B = make_uint4(and_or(w, 0x000F000Fu, 0x64006400u), and_or(w >> 4, 0x000F000Fu, 0x64006400u),
+                                   and_or(w >> 8, 0x000F000Fu, 0x64006400u), and_or(w >> 12, 0x000F000Fu, 0x64006400u));
+#pragma unroll
+        for (int r = 0; r < MB; ++r) T[r][cb] = mfma(s.av[r][t], B, T[r][cb]);
+      }
+#pragma unroll
+      for (int r = 0; r < MB; ++r) S[r] = mfma(s.av[r][t], ONES, S[r]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      float sc = 1.f, c = BIAS;
+      if constexpr (SCALED) sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(s.sc[cb] & 0xFFFFu));
+      if constexpr (ZEROS) c += (float)__builtin_bit_cast(_Float16, (uint16_t)(s.sc[cb] >> 16));
+#pragma unroll
+      for (int r = 0; r < MB; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[r][cb][i] += sc * (T[r][cb][i] - c * S[r][i]);
+    }
+  };
+
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  Stage s0, s1;
+  if (cnt > 0) {
+    int j = 0;
+    load(s0, 0);
+    for (; j + 2 < cnt; j += 2) {
+      fence();
+      load(s1, j + 1);
+      fence();
+      consume(s0);
+      fence();
+      load(s0, j + 2);
+      fence();
+      consume(s1);
+    }
+    fence();
+    if (j + 1 < cnt) {
+      load(s1, j + 1);
+      fence();
+      consume(s0);
+      fence();
+      consume(s1);
+    } else {
+      consume(s0);
+    }
+  }
+
+  // lane l holds rows 16 r + 4 (l / 16) + i of column l % 16 of each column block;
+  // the waves meet in LDS
+  __shared__ float red[GEMV_MAX_WAVES][MB][4][4][64];
+#pragma unroll
+  for (int r = 0; r < MB; ++r)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][r][cb][i][lane] = acc[r][cb][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MB * 4 * 4 * 64; idx += blockDim.x) {
+    const int r = idx >> 10, cb = (idx >> 8) & 3, i = (idx >> 6) & 3, ln = idx & 63;
+    const int row = r * 16 + 4 * (ln >> 4) + i, col = rb * 64 + cb * 16 + (ln & 15);
+    if (row >= a.M || col >= a.N) continue;
+    float v = 0.f;
+    for (int w = 0; w < a.waves; ++w) v += red[w][r][cb][i][ln];
+    const size_t o = (size_t)row * a.N + col;
+    if (a.out_mode == OUT_STORE) static_cast<_Float16*>(a.C)[o] = (_Float16)(v + bias_f(a, col));
+    else if (a.out_mode == OUT_ATOMIC) unsafeAtomicAdd(static_cast<float*>(a.ws) + o, v);
+    else static_cast<float*>(a.ws)[(size_t)part * a.M * a.N + o] = v;
+  }
+}
+
+template <int FMT, int MB>
+hipError_t launch_mb(const RunArgs& a, hipStream_t st) {
+  const dim3 grid((a.N + 63) / 64, a.k_parts), block(64 * a.waves);
+  const int var = a.smode == SC_NONE ? 0 : a.zeros ? 2 : 1;
+  if (var == 0) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT, MB, 0>), grid, block, 0, st, a);
+  else if (var == 1) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT, MB, 1>), grid, block, 0, st, a);
+  else if (FMT == FMT_U4) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT_U4, MB, 2>), grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_mfma4(int fmt, const RunArgs& a, hipStream_t st) {
+  if (a.M < 1 || a.M > 32 || a.smode == SC_PIECE) return hipErrorInvalidValue;
+  if (fmt == FMT_I4) return a.M <= 16 ? launch_mb<FMT_I4, 1>(a, st) : launch_mb<FMT_I4, 2>(a, st);
+  if (fmt == FMT_U4) return a.M <= 16 ? launch_mb<FMT_U4, 1>(a, st) : launch_mb<FMT_U4, 2>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qg

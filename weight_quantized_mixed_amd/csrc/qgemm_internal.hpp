@@ -115,6 +115,8 @@ hipError_t launch_gemv(int fmt, const RunArgs& a, hipStream_t st);
 hipError_t launch_gemv16(int fmt, const RunArgs& a, hipStream_t st);
 // int8 / int2 skinny-M on the matrix cores, B operands straight from the blob (gemv_mfma.hip)
 hipError_t launch_gemv_mfma(int fmt, const RunArgs& a, hipStream_t st);
+// int4 / uint4 skinny-M (M <= 32) on the matrix cores, bias-folded B operands (gemv_mfma4.hip)
+hipError_t launch_gemv_mfma4(int fmt, const RunArgs& a, hipStream_t st);
 hipError_t launch_mfma(int fmt, int tile, const RunArgs& a, hipStream_t st);
 // direct-load ring kernel (mfma_dl.hip): the tile for a problem, or -1 when the
 // problem needs the LDS-staged kernel (int4 with per-piece scale groups)
