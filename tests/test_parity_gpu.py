@@ -55,6 +55,11 @@ SMALL = [
     (32, 520, 1024, "u4", 128, True),
     (12, 136, 512, "i4", 0, False),
     (24, 72, 1536, "u4", 384, True),
+    # int8 / int2 rows 9..32 on the matrix cores (two row blocks past 16)
+    (16, 200, 2048, "i2", 0, False),
+    (17, 136, 1024, "i2", 0, False),
+    (32, 264, 2048, "i2", 0, False),
+    (24, 520, 512, "i8", 0, False),
     # int8 / int2 rows 2..8 on the matrix cores (ragged last 64-column block)
     (2, 200, 1024, "i8", 0, False),
     (3, 72, 2048, "i2", 0, False),

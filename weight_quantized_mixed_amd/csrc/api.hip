@@ -67,15 +67,19 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
 }
 
 // formats (bit per format) whose GEMV runs on the matrix cores (int8, int2 only),
-// from this many rows on: the matrix cores take up to 16 rows for the price of
-// one (W2A8 M = 8: 13.9 us against 31.5 us with dot products), while at M = 1 the
-// dot-product GEMV reads its activations through the scalar unit and stays
-// ahead (12.6 against 13.2 us)
+// for M in [MIN_M, MAX_M]: the matrix cores take up to 16 rows for the price of
+// one (W2A8 M = 8: 13.9 us against 31.5 us with dot products; M = 16 / 24 / 32:
+// 17.1 / 22.0 / 25.3 us against 30.9 / 31.9 / 31.4 us with the direct-load
+// kernel), while at M = 1 the dot-product GEMV reads its activations through the
+// scalar unit and stays ahead (12.6 against 13.2 us)
 #ifndef QG_GEMV_MFMA_FMTS
 #define QG_GEMV_MFMA_FMTS ((1 << FMT_I8) | (1 << FMT_I2))
 #endif
 #ifndef QG_GEMV_MFMA_MIN_M
 #define QG_GEMV_MFMA_MIN_M 2
+#endif
+#ifndef QG_GEMV_MFMA_MAX_M
+#define QG_GEMV_MFMA_MAX_M 32
 #endif
 // rows for which int4 / uint4 (groups of whole superblocks) take the matrix-core
 // GEMV instead of the dot-product GEMV (M <= 8) or the direct-load kernel.
@@ -147,7 +151,7 @@ qg_choice choose(const qgemm_plan* p, int64_t M) {
                                                           scale_mode(p->L.fmt, p->group_size))
                                         : -1;
   c.gemv_narrow = c.path == QGEMM_PATH_GEMV && choose_gemv_narrow(p, M);
-  c.gemv_mfma = c.path == QGEMM_PATH_GEMV && !c.gemv_narrow && M >= QG_GEMV_MFMA_MIN_M &&
+  c.gemv_mfma = !c.gemv_narrow && M >= QG_GEMV_MFMA_MIN_M && M <= QG_GEMV_MFMA_MAX_M &&
                 ((QG_GEMV_MFMA_FMTS >> p->L.fmt) & 1);
   const int smode = scale_mode(p->L.fmt, p->group_size);
   c.gemv_mfma4 = (p->L.fmt == FMT_I4 || p->L.fmt == FMT_U4) && !c.gemv_narrow && smode != SC_PIECE &&
@@ -224,9 +228,9 @@ qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const vo
                 : launch_fill_zero(C, (size_t)M * plan->N * 4, st);
   if (e == hipSuccess)
     e = ch.gemv_mfma4 ? launch_gemv_mfma4(plan->L.fmt, a, st)
+        : ch.gemv_mfma ? launch_gemv_mfma(plan->L.fmt, a, st)
         : ch.path == QGEMM_PATH_GEMV ? (ch.gemv_narrow ? launch_gemv16(plan->L.fmt, a, st)
-                                      : ch.gemv_mfma  ? launch_gemv_mfma(plan->L.fmt, a, st)
-                                                      : launch_gemv(plan->L.fmt, a, st))
+                                                       : launch_gemv(plan->L.fmt, a, st))
         : ch.dl_tile >= 0 ? launch_mfma_dl(plan->L.fmt, ch.dl_tile, a, st)
         : launch_mfma(plan->L.fmt, ch.tile, a, st);
   if (e == hipSuccess && (a.out_mode == OUT_PARTIAL || (a.out_mode == OUT_ATOMIC && out_f16)))

@@ -1,4 +1,4 @@
-// Skinny-M int8 / int2 path on the matrix cores (M <= 8).
+// Skinny-M int8 / int2 path on the matrix cores (M <= 32).
 //
 // The packed blob already holds every 16-column superblock in the lane order of
 // a gfx950 16x16 MFMA B operand (lane l: column l % 16, K group l / 16), so one
@@ -8,7 +8,8 @@
 // take the part's superblock rows in turn (as the VALU GEMV does) and meet in
 // LDS at the end.  The activation rows ride in the A operand: lane l loads the
 // K group l / 16 of row l % 16 (rows past M repeat row M - 1, and their results
-// are dropped), so up to 16 rows cost the same instructions as one.
+// are dropped), so up to 16 rows cost the same instructions as one; a second row
+// block of 16 reuses every B operand.
 //
 // int8: one v_mfma_i32_16x16x64_i8 per superblock and column block.
 // int2: word t of piece g holds positions 64 g + 16 t + 4 j + b (class j, byte b);
@@ -52,16 +53,24 @@ __device__ __forceinline__ int4v masked(const uint4& w, uint32_t m) {
   return int4v{(int)(w.x & m), (int)(w.y & m), (int)(w.z & m), (int)(w.w & m)};
 }
 
+__device__ __forceinline__ int4v shifted_masked(const uint4& w, int sh, uint32_t m) {
+  return int4v{(int)((w.x >> sh) & m), (int)((w.y >> sh) & m), (int)((w.z >> sh) & m), (int)((w.w >> sh) & m)};
+}
+
 __device__ __forceinline__ int4v mfma(const int4v& A, const int4v& B, const int4v& C) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, C, 0, 0, 0);
 }
 
-template <int FMT>
+// MB row blocks of 16 (M <= 16 MB)
+template <int FMT, int MB>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs a) {
   constexpr bool I2 = FMT == FMT_I2;
   constexpr int KB = kb_of(FMT);   // positions per superblock: 256 (int2), 64 (int8)
   constexpr int AV = KB / 64;      // 16-byte activation vectors per lane and superblock
-  constexpr int NC = I2 ? 4 : 1;   // MFMAs per column block and superblock (int2 classes)
+  // accumulators per column block: int2 keeps the four classes apart (values 4^j c)
+  // with one row block; with two (registers) it shifts classes 1 and 2 down to c
+  // and sums classes 0-2 in one accumulator, the two's complement class in another
+  constexpr int NC = !I2 ? 1 : MB == 1 ? 4 : 2;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -81,54 +90,79 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
   // rows past M read row M - 1 (results dropped): the loads stay unconditional,
   // since masking them off makes the compiler drain every load in flight at the
   // end of the masked block.
-  const uint4* __restrict__ Al =
-      reinterpret_cast<const uint4*>(static_cast<const int8_t*>(a.A) + (size_t)min(r16, a.M - 1) * a.K) + g * AV;
+  const uint4* __restrict__ Al[MB];
+#pragma unroll
+  for (int r = 0; r < MB; ++r)
+    Al[r] = reinterpret_cast<const uint4*>(static_cast<const int8_t*>(a.A) + (size_t)min(r * 16 + r16, a.M - 1) * a.K) +
+            g * AV;
 
   // A is loaded before the weights, so that waiting for a stage's activations
   // never waits for the weight loads of the stage after it
   struct Stage {
-    uint4 av[AV];
+    uint4 av[MB][AV];
     uint4 w[4];
   };
   auto load = [&](Stage& s, int j) {
     const uint32_t kb = (uint32_t)row_of(min(j, cnt - 1));
 #pragma unroll
-    for (int i = 0; i < AV; ++i) s.av[i] = load16(Al + kb * (KB / 16) + i);
+    for (int r = 0; r < MB; ++r)
+#pragma unroll
+      for (int i = 0; i < AV; ++i) s.av[r][i] = load16(Al[r] + kb * (KB / 16) + i);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) s.w[cb] = stream_load(Wl + kb * sb_stride + cb * 64);
   };
 
-  int4v acc[4][NC];
+  int4v acc[MB][4][NC];
+  int4v accS[MB];  // int2: activation sums of classes 0-2
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int r = 0; r < MB; ++r) {
+    accS[r] = int4v{0, 0, 0, 0};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[cb][c] = int4v{0, 0, 0, 0};
-  int4v accS = int4v{0, 0, 0, 0};  // int2: activation sums of classes 0-2
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[r][cb][c] = int4v{0, 0, 0, 0};
+  }
 
   auto consume = [&](const Stage& s) {
-    if constexpr (I2) {
-      // the A operand of class j takes dword 4 t + j of the lane's 64-byte slice as
-      // its dword t
-      int4v A[4];
-      A[0] = int4v{mv(s.av[0].x), mv(s.av[1].x), mv(s.av[2].x), mv(s.av[3].x)};
-      A[1] = int4v{mv(s.av[0].y), mv(s.av[1].y), mv(s.av[2].y), mv(s.av[3].y)};
-      A[2] = int4v{mv(s.av[0].z), mv(s.av[1].z), mv(s.av[2].z), mv(s.av[3].z)};
-      A[3] = int4v{mv(s.av[0].w), mv(s.av[1].w), mv(s.av[2].w), mv(s.av[3].w)};
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const uint4 w = s.w[cb];
-        acc[cb][0] = mfma(A[0], masked(w, 0x03030303u), acc[cb][0]);
-        acc[cb][1] = mfma(A[1], masked(w, 0x0C0C0C0Cu), acc[cb][1]);
-        acc[cb][2] = mfma(A[2], masked(w, 0x30303030u), acc[cb][2]);
-        acc[cb][3] = mfma(A[3], masked(w, 0xC0C0C0C0u), acc[cb][3]);
+    for (int r = 0; r < MB; ++r) {
+      if constexpr (I2) {
+        // the A operand of class j takes dword 4 t + j of the lane's 64-byte slice as
+        // its dword t
+        int4v A[4];
+        A[0] = int4v{mv(s.av[r][0].x), mv(s.av[r][1].x), mv(s.av[r][2].x), mv(s.av[r][3].x)};
+        A[1] = int4v{mv(s.av[r][0].y), mv(s.av[r][1].y), mv(s.av[r][2].y), mv(s.av[r][3].y)};
+        A[2] = int4v{mv(s.av[r][0].z), mv(s.av[r][1].z), mv(s.av[r][2].z), mv(s.av[r][3].z)};
+        A[3] = int4v{mv(s.av[r][0].w), mv(s.av[r][1].w), mv(s.av[r][2].w), mv(s.av[r][3].w)};
+        if constexpr (NC == 4) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const uint4 w = s.w[cb];
+            acc[r][cb][0] = mfma(A[0], masked(w, 0x03030303u), acc[r][cb][0]);
+            acc[r][cb][1] = mfma(A[1], masked(w, 0x0C0C0C0Cu), acc[r][cb][1]);
+            acc[r][cb][2] = mfma(A[2], masked(w, 0x30303030u), acc[r][cb][2]);
+            acc[r][cb][3] = mfma(A[3], masked(w, 0xC0C0C0C0u), acc[r][cb][3]);
+          }
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc[r][cb][0] = mfma(A[0], masked(s.w[cb], 0x03030303u), acc[r][cb][0]);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            acc[r][cb][0] = mfma(A[1], shifted_masked(s.w[cb], 2, 0x03030303u), acc[r][cb][0]);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            acc[r][cb][0] = mfma(A[2], shifted_masked(s.w[cb], 4, 0x03030303u), acc[r][cb][0]);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc[r][cb][1] = mfma(A[3], masked(s.w[cb], 0xC0C0C0C0u), acc[r][cb][1]);
+        }
+        const int4v ones = int4v{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+        accS[r] = mfma(A[0], ones, accS[r]);
+        accS[r] = mfma(A[1], ones, accS[r]);
+        accS[r] = mfma(A[2], ones, accS[r]);
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[r][cb][0] = mfma(as_i4(s.av[r][0]), as_i4(s.w[cb]), acc[r][cb][0]);
       }
-      const int4v ones = int4v{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-      accS = mfma(A[0], ones, accS);
-      accS = mfma(A[1], ones, accS);
-      accS = mfma(A[2], ones, accS);
-    } else {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[cb][0] = mfma(as_i4(s.av[0]), as_i4(s.w[cb]), acc[cb][0]);
     }
   };
 
@@ -162,25 +196,29 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
     }
   }
 
-  // lane l holds rows 4 (l / 16) + r of column l % 16 of each column block; the
-  // waves meet in LDS
-  __shared__ int red[GEMV_MAX_WAVES][4][4][64];
+  // lane l holds rows 16 rb + 4 (l / 16) + i of column l % 16 of each column block;
+  // the waves meet in LDS
+  __shared__ int red[GEMV_MAX_WAVES][MB][4][4][64];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int r = 0; r < MB; ++r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int v = acc[cb][0][r];
-      if constexpr (I2)  // classes 0..2 are offset-binary (q + 2)
-        v += (acc[cb][1][r] >> 2) + (acc[cb][2][r] >> 4) + (acc[cb][3][r] >> 6) - 2 * accS[r];
-      red[wave][cb][r][lane] = v;
-    }
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int v = acc[r][cb][0][i];
+        if constexpr (NC == 4)  // classes 0..2 are offset-binary (q + 2)
+          v += (acc[r][cb][1][i] >> 2) + (acc[r][cb][2][i] >> 4) + (acc[r][cb][3][i] >> 6) - 2 * accS[r][i];
+        else if constexpr (NC == 2)
+          v += (acc[r][cb][1][i] >> 6) - 2 * accS[r][i];
+        red[wave][r][cb][i][lane] = v;
+      }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 4 * 4 * 64; idx += blockDim.x) {
-    const int cb = idx >> 8, r = (idx >> 6) & 3, ln = idx & 63;
-    const int row = 4 * (ln >> 4) + r, col = rb * 64 + cb * 16 + (ln & 15);
+  for (int idx = threadIdx.x; idx < MB * 4 * 4 * 64; idx += blockDim.x) {
+    const int r = idx >> 10, cb = (idx >> 8) & 3, i = (idx >> 6) & 3, ln = idx & 63;
+    const int row = r * 16 + 4 * (ln >> 4) + i, col = rb * 64 + cb * 16 + (ln & 15);
     if (row >= a.M || col >= a.N) continue;
     int s = 0;
-    for (int w = 0; w < a.waves; ++w) s += red[w][cb][r][ln];
+    for (int w = 0; w < a.waves; ++w) s += red[w][r][cb][i][ln];
     const size_t o = (size_t)row * a.N + col;
     if (a.out_mode == OUT_STORE) {
       if (a.row_scale) static_cast<_Float16*>(a.C)[o] = dq_out(a, row, col, s);
@@ -196,11 +234,18 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
 }  // namespace
 
 hipError_t launch_gemv_mfma(int fmt, const RunArgs& a, hipStream_t st) {
-  if (a.M < 1 || a.M > 16) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > 32) return hipErrorInvalidValue;
   const dim3 grid((a.N + 63) / 64, a.k_parts), block(64 * a.waves);
-  if (fmt == FMT_I8) hipLaunchKernelGGL(gemv_mfma_kernel<FMT_I8>, grid, block, 0, st, a);
-  else if (fmt == FMT_I2) hipLaunchKernelGGL(gemv_mfma_kernel<FMT_I2>, grid, block, 0, st, a);
-  else return hipErrorInvalidValue;
+  const bool two = a.M > 16;
+  if (fmt == FMT_I8) {
+    if (two) hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I8, 2>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I8, 1>), grid, block, 0, st, a);
+  } else if (fmt == FMT_I2) {
+    if (two) hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I2, 2>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I2, 1>), grid, block, 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
