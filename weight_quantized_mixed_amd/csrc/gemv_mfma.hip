@@ -1,4 +1,4 @@
-// Skinny-M int8 / int2 path on the matrix cores (M <= 32).
+// Skinny-M int8 / int2 / fp16 path on the matrix cores (M <= 32).
 //
 // The packed blob already holds every 16-column superblock in the lane order of
 // a gfx950 16x16 MFMA B operand (lane l: column l % 16, K group l / 16), so one
@@ -11,7 +11,8 @@
 // are dropped), so up to 16 rows cost the same instructions as one; a second row
 // block of 16 reuses every B operand.
 //
-// int8: one v_mfma_i32_16x16x64_i8 per superblock and column block.
+// int8: one v_mfma_i32_16x16x64_i8 per superblock and column block; fp16 the same
+// with v_mfma_f32_16x16x32_f16 (a 32-position superblock, fp32 accumulation).
 // int2: word t of piece g holds positions 64 g + 16 t + 4 j + b (class j, byte b);
 // masking word t with 0x03, 0x0C, 0x30 or 0xC0 per byte keeps class j as the byte
 // value 4^j c (the top class two's complement, so 64 q as a signed byte), and the
@@ -21,12 +22,16 @@
 // against a B of ones gives the activation sums that the correction subtracts.
 // Per word this is four VALU masks, where the dot-product GEMV needs four masks
 // and four dot products.
+#include <type_traits>
+
 #include "qgemm_internal.hpp"
 
 namespace qg {
 namespace {
 
 typedef int int4v __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint4 stream_load(const uint4* p) {
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -61,12 +66,20 @@ __device__ __forceinline__ int4v mfma(const int4v& A, const int4v& B, const int4
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, C, 0, 0, 0);
 }
 
+// fp16 weights: 16x16x32 with fp32 accumulation
+__device__ __forceinline__ float4v mfma(const int4v& A, const int4v& B, const float4v& C) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8v, A), __builtin_bit_cast(half8v, B), C, 0, 0, 0);
+}
+
 // MB row blocks of 16 (M <= 16 MB)
 template <int FMT, int MB>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs a) {
-  constexpr bool I2 = FMT == FMT_I2;
-  constexpr int KB = kb_of(FMT);   // positions per superblock: 256 (int2), 64 (int8)
-  constexpr int AV = KB / 64;      // 16-byte activation vectors per lane and superblock
+  constexpr bool I2 = FMT == FMT_I2, FP = FMT == FMT_F16;
+  constexpr int KB = kb_of(FMT);   // positions per superblock: 256 (int2), 64 (int8), 32 (fp16)
+  constexpr int ESZ = FP ? 2 : 1;  // activation bytes
+  constexpr int AV = KB * ESZ / 64;  // 16-byte activation vectors per lane and superblock
+  typedef typename std::conditional<FP, float4v, int4v>::type acc_v;
+  typedef typename std::conditional<FP, float, int>::type acc_t;
   // accumulators per column block: int2 keeps the four classes apart (values 4^j c)
   // with one row block; with two (registers) it shifts classes 1 and 2 down to c
   // and sums classes 0-2 in one accumulator, the two's complement class in another
@@ -93,7 +106,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
   const uint4* __restrict__ Al[MB];
 #pragma unroll
   for (int r = 0; r < MB; ++r)
-    Al[r] = reinterpret_cast<const uint4*>(static_cast<const int8_t*>(a.A) + (size_t)min(r * 16 + r16, a.M - 1) * a.K) +
+    Al[r] = reinterpret_cast<const uint4*>(static_cast<const int8_t*>(a.A) +
+                                           (size_t)min(r * 16 + r16, a.M - 1) * a.K * ESZ) +
             g * AV;
 
   // A is loaded before the weights, so that waiting for a stage's activations
@@ -107,12 +121,12 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
 #pragma unroll
     for (int r = 0; r < MB; ++r)
 #pragma unroll
-      for (int i = 0; i < AV; ++i) s.av[r][i] = load16(Al[r] + kb * (KB / 16) + i);
+      for (int i = 0; i < AV; ++i) s.av[r][i] = load16(Al[r] + kb * (KB * ESZ / 16) + i);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) s.w[cb] = stream_load(Wl + kb * sb_stride + cb * 64);
   };
 
-  int4v acc[MB][4][NC];
+  acc_v acc[MB][4][NC];
   int4v accS[MB];  // int2: activation sums of classes 0-2
 #pragma unroll
   for (int r = 0; r < MB; ++r) {
@@ -120,7 +134,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[r][cb][c] = int4v{0, 0, 0, 0};
+      for (int c = 0; c < NC; ++c) acc[r][cb][c] = acc_v{0, 0, 0, 0};
   }
 
   auto consume = [&](const Stage& s) {
@@ -198,14 +212,14 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
 
   // lane l holds rows 16 rb + 4 (l / 16) + i of column l % 16 of each column block;
   // the waves meet in LDS
-  __shared__ int red[GEMV_MAX_WAVES][MB][4][4][64];
+  __shared__ acc_t red[GEMV_MAX_WAVES][MB][4][4][64];
 #pragma unroll
   for (int r = 0; r < MB; ++r)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int v = acc[r][cb][0][i];
+        acc_t v = acc[r][cb][0][i];
         if constexpr (NC == 4)  // classes 0..2 are offset-binary (q + 2)
           v += (acc[r][cb][1][i] >> 2) + (acc[r][cb][2][i] >> 4) + (acc[r][cb][3][i] >> 6) - 2 * accS[r][i];
         else if constexpr (NC == 2)
@@ -217,16 +231,22 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
     const int r = idx >> 10, cb = (idx >> 8) & 3, i = (idx >> 6) & 3, ln = idx & 63;
     const int row = r * 16 + 4 * (ln >> 4) + i, col = rb * 64 + cb * 16 + (ln & 15);
     if (row >= a.M || col >= a.N) continue;
-    int s = 0;
+    acc_t s = 0;
     for (int w = 0; w < a.waves; ++w) s += red[w][r][cb][i][ln];
     const size_t o = (size_t)row * a.N + col;
-    if (a.out_mode == OUT_STORE) {
-      if (a.row_scale) static_cast<_Float16*>(a.C)[o] = dq_out(a, row, col, s);
-      else static_cast<int*>(a.C)[o] = s + bias_i(a, col);
-    } else if (a.out_mode == OUT_ATOMIC) {
-      atomicAdd(int_atomic_target(a) + o, s);
+    if constexpr (FP) {
+      if (a.out_mode == OUT_STORE) static_cast<_Float16*>(a.C)[o] = (_Float16)(s + bias_f(a, col));
+      else if (a.out_mode == OUT_ATOMIC) unsafeAtomicAdd(static_cast<float*>(a.ws) + o, s);
+      else static_cast<float*>(a.ws)[(size_t)part * a.M * a.N + o] = s;
     } else {
-      static_cast<int*>(a.ws)[(size_t)part * a.M * a.N + o] = s;
+      if (a.out_mode == OUT_STORE) {
+        if (a.row_scale) static_cast<_Float16*>(a.C)[o] = dq_out(a, row, col, s);
+        else static_cast<int*>(a.C)[o] = s + bias_i(a, col);
+      } else if (a.out_mode == OUT_ATOMIC) {
+        atomicAdd(int_atomic_target(a) + o, s);
+      } else {
+        static_cast<int*>(a.ws)[(size_t)part * a.M * a.N + o] = s;
+      }
     }
   }
 }
@@ -243,6 +263,9 @@ hipError_t launch_gemv_mfma(int fmt, const RunArgs& a, hipStream_t st) {
   } else if (fmt == FMT_I2) {
     if (two) hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I2, 2>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I2, 1>), grid, block, 0, st, a);
+  } else if (fmt == FMT_F16) {
+    if (two) hipLaunchKernelGGL((gemv_mfma_kernel<FMT_F16, 2>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gemv_mfma_kernel<FMT_F16, 1>), grid, block, 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }
