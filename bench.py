@@ -207,7 +207,10 @@ def measure_grid_entry(b, bursts=50):
     so that small calls are timed on the GPU rather than at the host's launch rate."""
     import statistics
     b.timed(5)
-    per = max(len(b.packed), 8)
+    # at least 64 calls per replay (whole turns of the ring), so that the replay's own
+    # start-up is spread over enough calls not to show in the per-call time
+    ring = max(len(b.packed), 1)
+    per = ring * max(1, -(-64 // ring))
     if b.flops > 1e12:
         per, bursts = 2, 5
     g = b.graph(per)

@@ -58,8 +58,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
   const int rb = blockIdx.x, part = blockIdx.y;
   const int g = lane >> 4, n16 = lane & 15;
 
-  const int u0 = (int)((int64_t)part * a.n_units / a.k_parts);
-  const int u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
+  int u0, u1;
+  part_units(a, part, u0, u1);
   const int kb0 = u0 * a.unit_kb, kb1 = u1 * a.unit_kb;
   const int cnt = __builtin_amdgcn_readfirstlane(kb1 - kb0 > wave ? (kb1 - kb0 - wave + a.waves - 1) / a.waves : 0);
   auto row_of = [&](int j) { return __builtin_amdgcn_readfirstlane(kb0 + wave + j * a.waves); };

@@ -88,8 +88,8 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma_kernel(RunArgs a) {
   const int in_group = w - group * GROUP_M * tiles_n;
   const int m0 = (first_m + in_group % gsz) * BM, n0 = (in_group / gsz) * BN;
 
-  const int u0 = (int)((int64_t)part * a.n_units / a.k_parts);
-  const int u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
+  int u0, u1;
+  part_units(a, part, u0, u1);
   const int kb0 = u0 * a.unit_kb, kb1 = u1 * a.unit_kb;
   const int nst = (kb1 - kb0 + KSTEP - 1) / KSTEP;
 

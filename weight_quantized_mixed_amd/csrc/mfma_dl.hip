@@ -229,8 +229,8 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
 
   // ---- stages of this k-part
   constexpr int SPB = KB / SPOS;  // stages per superblock
-  const int u0 = (int)((int64_t)part * a.n_units / a.k_parts);
-  const int u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
+  int u0, u1;
+  part_units(a, part, u0, u1);
   const int s0 = u0 * a.unit_kb * SPB, s1 = u1 * a.unit_kb * SPB;  // global stage indices
   const int nst = s1 - s0;
 

@@ -107,6 +107,18 @@ __device__ __forceinline__ int* int_atomic_target(const RunArgs& a) {
   return static_cast<int*>(a.row_scale ? a.ws : a.C);
 }
 
+// Split units [u0, u1) of K part `part` (contiguous, as even as integers allow).
+// Without a split the 64-bit division, which costs a measurable part of a
+// microsecond-scale kernel's start, is skipped.
+__device__ __forceinline__ void part_units(const RunArgs& a, int part, int& u0, int& u1) {
+  u0 = 0;
+  u1 = a.n_units;
+  if (a.k_parts != 1) {
+    u0 = (int)((int64_t)part * a.n_units / a.k_parts);
+    u1 = (int)((int64_t)(part + 1) * a.n_units / a.k_parts);
+  }
+}
+
 // kernel launchers (return hipSuccess or the launch error)
 hipError_t launch_pack(const Layout& L, const void* w, const void* s, const void* z, void* packed,
                        hipStream_t st);
