@@ -207,13 +207,15 @@ def test_big_tile_parity(M, N, K, w_dtype, g, zeros, kp, det):
 
 
 # ---------------------------------------------------------------- direct-load tiles of every shape
-# The tile is the largest one within M's power-of-two row cap that still gives >= 256
-# workgroups (N / BN x M / BM x k_parts), so these shapes select, in order:
-# 32x64, 32x128, 32x256, 64x128, 64x256, 128x256, 256x256 (rows and columns ragged).
+# The tile is the largest one within M's power-of-two row cap whose last wave of
+# workgroups (N / BN x M / BM x k_parts) still occupies 60 % of the 256 CUs, so these
+# shapes select, in order: 32x64, 32x128, 32x256 (int4 / uint4 without scales; the
+# other formats take the matrix-core GEMV up to 32 rows), 64x128, 64x256, 128x256,
+# 256x256, and 128x128 (int4 / uint4 / int2; rows and columns ragged).
 DL_SHAPES = [(20, 16376, 1, False), (20, 16376, 2, True), (20, 16376, 4, False), (40, 16376, 2, False),
-             (40, 16376, 4, True), (100, 16376, 4, False), (300, 16376, 2, True)]
-DL_FORMATS = [("i4", 128, False), ("u4", 128, True), ("u4", 256, False), ("f16", 0, False), ("i8", 0, False),
-              ("i2", 0, False)]
+             (40, 16376, 4, True), (100, 16376, 4, False), (300, 16376, 2, True), (100, 24000, 1, False)]
+DL_FORMATS = [("i4", 128, False), ("u4", 128, True), ("u4", 256, False), ("i4", 0, False), ("f16", 0, False),
+              ("i8", 0, False), ("i2", 0, False)]
 
 
 @pytest.mark.parametrize("M,N,kp,det", DL_SHAPES)

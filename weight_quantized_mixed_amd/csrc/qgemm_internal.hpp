@@ -132,7 +132,9 @@ hipError_t launch_gemv_mfma4(int fmt, const RunArgs& a, hipStream_t st);
 hipError_t launch_mfma(int fmt, int tile, const RunArgs& a, hipStream_t st);
 // direct-load ring kernel (mfma_dl.hip): the tile for a problem, or -1 when the
 // problem needs the LDS-staged kernel (int4 with per-piece scale groups)
-enum DlTile : int { DL_32x64 = 0, DL_32x128, DL_32x256, DL_64x128, DL_64x256, DL_128x256, DL_256x256, DL_NUM };
+enum DlTile : int {
+  DL_32x64 = 0, DL_32x128, DL_32x256, DL_64x128, DL_64x256, DL_128x256, DL_256x256, DL_128x128, DL_NUM
+};
 void dl_tile_dims(int tile, int* bm, int* bn);
 int choose_dl_tile(int fmt, int64_t M, int64_t N, int k_parts, int smode);
 hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st);
