@@ -48,7 +48,10 @@ SMALL = [
     (70, 136, 1920, "i4", 96, False),
     (40, 264, 1536, "u4", 384, True),
     (300, 520, 1536, "i4", 384, False),
-    # int4 / uint4 rows 5..32 on the matrix cores (bias-folded operands, per-superblock fold)
+    # int4 / uint4 rows 3..32 on the matrix cores (bias-folded operands, per-superblock fold)
+    (4, 520, 2048, "i4", 0, False),
+    (3, 136, 1024, "u4", -1, True),
+    (28, 200, 1024, "i4", 0, False),
     (5, 200, 1024, "i4", 128, False),
     (16, 264, 1024, "u4", 128, True),
     (17, 300, 2048, "i4", -1, False),
@@ -208,12 +211,13 @@ def test_big_tile_parity(M, N, K, w_dtype, g, zeros, kp, det):
 
 # ---------------------------------------------------------------- direct-load tiles of every shape
 # The tile is the largest one within M's power-of-two row cap whose last wave of
-# workgroups (N / BN x M / BM x k_parts) still occupies 60 % of the 256 CUs, so these
-# shapes select, in order: 32x64, 32x128, 32x256 (int4 / uint4 without scales; the
-# other formats take the matrix-core GEMV up to 32 rows), 64x128, 64x256, 128x256,
-# 256x256, and 128x128 (int4 / uint4 / int2; rows and columns ragged).
-DL_SHAPES = [(20, 16376, 1, False), (20, 16376, 2, True), (20, 16376, 4, False), (40, 16376, 2, False),
-             (40, 16376, 4, True), (100, 16376, 4, False), (300, 16376, 2, True), (100, 24000, 1, False)]
+# workgroups (N / BN x M / BM x k_parts) still occupies 60 % of the 256 CUs; up to 32
+# rows every format takes a matrix-core GEMV instead.  These shapes select, in order:
+# 32x64, 32x128 (33..64 rows and few columns), 64x128, 64x256, 128x256, 256x256,
+# 128x128 (int4 / uint4 / int2; 64x256 for the others), and the skinny matrix-core
+# GEMV with k_parts 4 (rows and columns ragged).
+DL_SHAPES = [(40, 1000, 1, False), (40, 12000, 1, False), (40, 16376, 2, False), (40, 16376, 4, True),
+             (100, 16376, 4, False), (300, 16376, 2, True), (100, 24000, 1, False), (20, 16376, 4, False)]
 DL_FORMATS = [("i4", 128, False), ("u4", 128, True), ("u4", 256, False), ("i4", 0, False), ("f16", 0, False),
               ("i8", 0, False), ("i2", 0, False)]
 

@@ -84,17 +84,18 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
 #endif
 // rows for which int4 / uint4 (groups of whole superblocks) take the matrix-core
 // GEMV instead of the dot-product GEMV (M <= 8) or the direct-load kernel.
-// Measured at N = K = 16384, g = 128: M = 2 / 4 / 8 / 16 / 32 ran 40.8 / 42.1 /
-// 44.3 / 48.1 / 63.4 us against 29.8 / 41.3 / 64.5 / 67.8 / 69.7 us; unscaled
-// (g = 0) the direct-load kernel keeps M = 32 (58.9 against 63.4 us).
+// Measured at N = K = 16384, g = 128: M = 4 / 8 / 16 / 32 ran 24.6 / 25.5 / 29.2 /
+// 42.4 us against 35.8 / 64.5 / 67.8 / 69.7 us; M = 2 ties with the dot-product
+// GEMV (24.5 us) and unscaled M = 2 is faster there (23.4 against 24.7 us); unscaled
+// M = 24 / 32 ran 37.1 / 41.4 us against 53.4 / 53.6 us with the direct-load kernel.
 #ifndef QG_GEMV4_MFMA_MIN_M
-#define QG_GEMV4_MFMA_MIN_M 5
+#define QG_GEMV4_MFMA_MIN_M 3
 #endif
 #ifndef QG_GEMV4_MFMA_MAX_M
 #define QG_GEMV4_MFMA_MAX_M 32
 #endif
 #ifndef QG_GEMV4_MFMA_MAX_M_UNSCALED
-#define QG_GEMV4_MFMA_MAX_M_UNSCALED 16
+#define QG_GEMV4_MFMA_MAX_M_UNSCALED 32
 #endif
 
 #ifndef QG_GEMV_TARGET_WAVES

@@ -1,12 +1,16 @@
-// Skinny-M int4 / uint4 path on the matrix cores (2 <= M <= 32).
+// Skinny-M int4 / uint4 path on the matrix cores (3 <= M <= 32).
 //
 // Lane l of a wave works on column l % 16 of a 16-column superblock and K group
 // g = l / 16 of every 32-position MFMA step.  In the packed blob, word g of the
 // piece of step s holds exactly that group's eight positions (nibble slots 0..7 =
-// positions 0,2,4,6,1,3,5,7), so the B operand of step s is four dword loads (one
-// per step, 256 contiguous bytes per wave) and four v_and_or_b32: slot pair
-// (jj, jj + 4) becomes the fp16 pair 1024 + q, with no subtraction (the bias
-// folding of the dot-product GEMV).  The A operand is a row of activations
+// positions 0,2,4,6,1,3,5,7).  A superblock is loaded as stored (one 16-byte load,
+// piece l for lane l: step l / 16, column l % 16), and a 4 x 4 transpose of dwords
+// across the four 16-lane rows (two permlane32 and two permlane16 swaps) hands
+// lane (g, c) word g of the piece of every step; four v_and_or_b32 then turn slot
+// pairs (jj, jj + 4) into the fp16 pairs 1024 + q, with no subtraction (the bias
+// folding of the dot-product GEMV).  (Loading the words one dword per step instead,
+// 16 loads of 256 bytes per wave for four superblocks, ran M = 8 in 40.9 against
+// 25.5 us.)  The A operand is a row of activations
 // (lane l: row l % 16 of the row block, positions 32 s + 8 g .. + 7), so one set
 // of B operands serves up to 16 rows per MFMA, two row blocks up to 32.
 //
@@ -34,7 +38,25 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 // for an inline-assembly writer
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
 
-__device__ __forceinline__ uint32_t stream_load32(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint4 stream_load16(const uint4* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// 4 x 4 transpose of dwords across the four 16-lane rows: lane (row r, column c)
+// holds x[w] = word w of row r's piece; afterwards x[t] = word r of row t's piece
+// (column c).  Two row-pair swaps, then two neighbouring-row swaps.
+__device__ __forceinline__ void transpose_rows(uint32_t (&x)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);  // rows 2,3 of x0 <-> rows 0,1 of x2
+  auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);  // odd rows of x0 <-> even rows of x1
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  x[0] = c[0];
+  x[1] = c[1];
+  x[2] = d[0];
+  x[3] = d[1];
+}
 
 __device__ __forceinline__ uint4 load16(const uint4* p) {
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -64,18 +86,18 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
   const int cnt = __builtin_amdgcn_readfirstlane(kb1 - kb0 > wave ? (kb1 - kb0 - wave + a.waves - 1) / a.waves : 0);
   auto row_of = [&](int j) { return __builtin_amdgcn_readfirstlane(kb0 + wave + j * a.waves); };
 
-  // word g of piece (s, n16) of superblock (kb, column block rb*4 + cb)
-  const uint32_t* __restrict__ Wd = reinterpret_cast<const uint32_t*>(a.W) + ((size_t)rb * 4 * 64 + n16) * 4 + g;
-  const uint32_t sb_stride = (uint32_t)a.NB * 256u;  // dwords per superblock row
   // activation rows of the lane (rows past M repeat row M - 1; results dropped)
   const uint4* __restrict__ Al[MB];
 #pragma unroll
   for (int r = 0; r < MB; ++r)
     Al[r] = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.A) + (size_t)min(r * 16 + n16, a.M - 1) * a.K) + g;
 
+  // piece l of each superblock (16 bytes) for lane l, as stored
+  const uint4* __restrict__ Wq = a.W + (size_t)rb * 4 * 64 + lane;
+  const uint32_t sbq_stride = (uint32_t)a.NB * 64u;  // uint4 per superblock row
   struct Stage {
     uint4 av[MB][NS];  // A operand of each row block and step
-    uint32_t w[4][NS];  // packed word of each column block and step
+    uint4 wq[4];        // piece (lane / 16, lane % 16) of each column block, as stored
     uint32_t sc[4];     // raw scale (| zero << 16) of each column block
   };
   auto load = [&](Stage& s, int j) {
@@ -85,9 +107,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
 #pragma unroll
       for (int t = 0; t < NS; ++t) s.av[r][t] = load16(Al[r] + kb * (KB / 8) + t * 4);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int t = 0; t < NS; ++t) s.w[cb][t] = stream_load32(Wd + kb * sb_stride + cb * 256 + t * 64);
+    for (int cb = 0; cb < 4; ++cb) s.wq[cb] = stream_load16(Wq + kb * sbq_stride + cb * 64);
     if constexpr (SCALED) {
       const uint32_t grp = a.sb_per_group == 1 ? kb : kb / (uint32_t)a.sb_per_group;
 #pragma unroll
@@ -107,6 +127,15 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
 
   const uint4 ONES = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
   auto consume = [&](const Stage& s) {
+    // packed word of each column block and step: word g of the piece of step t
+    uint32_t w[4][NS];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      uint32_t x[4] = {s.wq[cb].x, s.wq[cb].y, s.wq[cb].z, s.wq[cb].w};
+      transpose_rows(x);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) w[cb][t] = x[t];
+    }
     float4v T[MB][4], S[MB];
 #pragma unroll
     for (int r = 0; r < MB; ++r) {
@@ -118,9 +147,9 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
     for (int t = 0; t < NS; ++t) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const uint32_t w = s.w[cb][t];
-        const uint4 B = make_uint4(and_or(w, 0x000F000Fu, 0x64006400u), and_or(w >> 4, 0x000F000Fu, 0x64006400u),
-                                   and_or(w >> 8, 0x000F000Fu, 0x64006400u), and_or(w >> 12, 0x000F000Fu, 0x64006400u));
+        const uint32_t wd = w[cb][t];
+        const uint4 B = make_uint4(and_or(wd, 0x000F000Fu, 0x64006400u), and_or(wd >> 4, 0x000F000Fu, 0x64006400u),
+                                   and_or(wd >> 8, 0x000F000Fu, 0x64006400u), and_or(wd >> 12, 0x000F000Fu, 0x64006400u));
 #pragma unroll
         for (int r = 0; r < MB; ++r) T[r][cb] = mfma(s.av[r][t], B, T[r][cb]);
       }
