@@ -75,9 +75,12 @@ class QGemm:
         self._ws = None
 
     def close(self):
-        if getattr(self, "plan", None):
-            _q.qgemm_destroy(self.plan)
+        plan = getattr(self, "plan", None)
+        if plan:
             self.plan = None
+            destroy = getattr(_q, "qgemm_destroy", None)
+            if callable(destroy):  # not at interpreter exit, when the module is torn down
+                destroy(plan)
 
     __del__ = close
 
