@@ -85,8 +85,10 @@ typedef enum {
 #define QGEMM_DETERMINISTIC 1u /* k_parts > 1: fixed-order two-pass reduction instead of atomics */
 
 /* execution path chosen by a plan (qgemm_plan_path) */
-#define QGEMM_PATH_GEMV 1 /* M <= 8: wavefront dot-product kernel, no matrix cores */
-#define QGEMM_PATH_MFMA 2 /* M > 8: LDS-staged MFMA tiles */
+#define QGEMM_PATH_GEMV 1 /* M <= 8: skinny kernels streaming the weights once (dot products at
+                             one row; matrix cores from 2 rows, 3 for int4) */
+#define QGEMM_PATH_MFMA 2 /* M > 8: matrix cores (skinny kernels up to 32 rows, then
+                             LDS-staged tiles) */
 
 /*
  * Create a plan.  No device call.
