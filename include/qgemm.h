@@ -102,7 +102,8 @@ typedef enum {
  *   has_zeros     0 or 1; 1 only with w_dtype U4 and group_size != 0.
  *   k_parts       >= 1: number of contiguous, group-aligned K ranges computed by
  *                 separate workgroups and reduced with fp32/int32 global atomics
- *                 (or two-pass, QGEMM_DETERMINISTIC).  At most K / unit, where
+ *                 or by ordered partials and one summing pass (always with
+ *                 QGEMM_DETERMINISTIC; see qgemm_run).  At most K / unit, where
  *                 unit = group_size when it is a multiple of the block depth
  *                 (and larger), else the block depth.
  *   flags         0 or QGEMM_DETERMINISTIC.
@@ -134,9 +135,11 @@ qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const voi
  *   workspace  device, >= workspace_bytes (may be NULL when that is 0),
  *              16-byte aligned; scratch for split-K partials, its contents on
  *              entry are ignored.
- * Split-K with atomics sums in an unspecified order: fp16 results may differ
- * in the last bits between runs; int32 results are exact.  With
- * QGEMM_DETERMINISTIC the result is bitwise reproducible.
+ * Split-K sums the parts in an order the library chooses per plan (ordered
+ * partials for fp16 outputs and for 128 rows or more whenever their workspace
+ * stays within 256 MiB, else atomics): results with atomics may differ in the
+ * last fp16 bits between runs, int32 results are exact either way.  With
+ * QGEMM_DETERMINISTIC the result is always bitwise reproducible.
  */
 qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed, void* C,
                        void* workspace, size_t workspace_bytes, void* stream);

@@ -96,15 +96,24 @@ def test_sizes_and_paths():
     plan, pb, wb = _create(M=9, N=100, k_parts=4)
     npad = 256
     assert pb == npad * 4096 // 2 + npad * 32 * 2
-    assert wb == 9 * 100 * 4                                # fp32 atomic accumulator
+    assert wb == 4 * 9 * 100 * 4                            # fp16 output: per-part partials
     assert q.qgemm_plan_path(plan) == q.QGEMM_PATH_MFMA
     q.qgemm_destroy(plan)
     plan, pb, wb = _create(M=9, N=100, k_parts=4, flags=q.QGEMM_DETERMINISTIC)
     assert wb == 4 * 9 * 100 * 4                            # per-part partials
     q.qgemm_destroy(plan)
-    plan, pb, wb = _create(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32",
-                           group_size=0, k_parts=4)
+    plan, pb, wb = _create(M=4100, N=8400, K=4096, k_parts=2)
+    assert wb == 4100 * 8400 * 4                            # partials past 256 MiB: fp32 atomics
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(M=4100, N=8400, K=4096, k_parts=2, flags=q.QGEMM_DETERMINISTIC)
+    assert wb == 2 * 4100 * 8400 * 4                        # deterministic: partials regardless
+    q.qgemm_destroy(plan)
+    i8 = dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0)
+    plan, pb, wb = _create(k_parts=4, **i8)
     assert wb == 0                                          # int32 atomics go straight into C
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(M=128, k_parts=4, **i8)
+    assert wb == 4 * 128 * 4096 * 4                         # 128 rows and more: partials
     q.qgemm_destroy(plan)
     plan, pb, wb = _create(w_dtype="u4", has_zeros=1, N=4096)
     assert pb == 4096 * 4096 // 2 + 32 * 4096 * 4           # (scale, zero) pairs
@@ -157,7 +166,7 @@ def test_null_and_misaligned_arguments_rejected_before_launch():
                         M=4, k_parts=2)
     i32, _, _ = _create(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0, M=4)
     try:
-        assert wb == 4 * 4096 * 4                              # int32 atomics go to the workspace
+        assert wb == 2 * 4 * 4096 * 4                          # fp16 output: per-part int32 partials
         for call in [lambda: q.qgemm_run(dq, 16, 16, 16, 16, wb, 0),
                      lambda: q.qgemm_run_ex(dq, 4, 16, 16, 0, 16, 16, wb, 0),
                      lambda: q.qgemm_run_scaled(dq, 4, 16, 16, 0, 16, 0, 16, 16, wb, 0),   # no row scales

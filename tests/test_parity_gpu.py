@@ -209,6 +209,21 @@ def test_big_tile_parity(M, N, K, w_dtype, g, zeros, kp, det):
                    f"big {w_dtype} M={M} N={N} kp={kp}")
 
 
+# fp16 outputs reduce split-K with ordered partials unless those would pass 256 MiB of
+# workspace; past it the atomic accumulator (zero fill, fp32 atomics, finalize) remains
+@pytest.mark.parametrize("w_dtype,g,zeros", [("i4", 128, False), ("u4", 128, True), ("f16", 0, False)])
+def test_atomic_split_past_the_partials_cap(w_dtype, g, zeros):
+    M, N, K = 4100, 8400, 256
+    say(f"atomic split M={M} N={N} K={K} {w_dtype} g={g} zeros={zeros} kp=2")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=2, seed=M + N + 17)
+    assert c.q.ws_bytes == M * N * 4
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.choice(M, 200, replace=False), [0, 255, 256, M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(N, 200, replace=False), [0, 255, 256, N - 1]]))
+    gpu = c.run()
+    assert_matches(gpu[np.ix_(rows, cols)], c.reference(rows=rows, cols=cols), f"atomic split {w_dtype}")
+
+
 # ---------------------------------------------------------------- direct-load tiles of every shape
 # The tile is the largest one within M's power-of-two row cap whose last wave of
 # workgroups (N / BN x M / BM x k_parts) still occupies 60 % of the 256 CUs; up to 32

@@ -29,6 +29,7 @@ struct qgemm_plan {
   Layout L;
   qg_choice ch;      // kernels for M rows (calls with fewer rows choose again)
   int32_t unit_kb, n_units;
+  bool two_pass;     // split-K reduced by partials + one ordered pass (else atomics)
   size_t ws_bytes;
 };
 
@@ -145,6 +146,27 @@ int scale_mode(int fmt, int32_t group_size) {
   return SC_BLOCK;
 }
 
+// Split-K reduction without QGEMM_DETERMINISTIC: the fixed-order two-pass form
+// (partials [k_parts][M][N], then one pass that sums them in part order) whenever
+// its workspace stays modest and it is faster, else atomics into one accumulator.
+// fp16 outputs go through an fp32 accumulator either way, and zero-filling it plus
+// contended fp32 atomics cost more than the partials (k_parts = 4: M = 1, LLaMA
+// shapes 10.5 -> 9.5 us; M = 128, N = 32000, K = 4096 105 -> 74 us; M = 512,
+// N = K = 16384 347 -> 291 us).  int32 outputs add atomically straight into C,
+// which wins below 128 rows (W2A8 M = 32: 34.2 against 37.9 us) and loses above
+// (W8A8 M = 512: 189 against 172 us).
+#ifndef QG_TWO_PASS_MAX_BYTES
+#define QG_TWO_PASS_MAX_BYTES ((size_t)256 << 20)
+#endif
+#ifndef QG_TWO_PASS_INT_MIN_M
+#define QG_TWO_PASS_INT_MIN_M 128
+#endif
+bool two_pass_split(int64_t M, size_t partial_bytes, bool out_f16, uint32_t flags) {
+  if (flags & QGEMM_DETERMINISTIC) return true;
+  if (partial_bytes > QG_TWO_PASS_MAX_BYTES) return false;
+  return out_f16 || M >= QG_TWO_PASS_INT_MIN_M;
+}
+
 qg_choice choose(const qgemm_plan* p, int64_t M) {
   qg_choice c;
   c.path = M <= 8 ? QGEMM_PATH_GEMV : QGEMM_PATH_MFMA;
@@ -194,7 +216,7 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
   a.n_units = p->n_units;
   a.waves = ch.gemv_waves;
   a.sb_per_group = p->group_size > KB ? p->group_size / KB : p->group_size < 0 ? (int32_t)p->L.nkb : 1;
-  a.out_mode = p->k_parts == 1 ? OUT_STORE : (p->flags & QGEMM_DETERMINISTIC) ? OUT_PARTIAL : OUT_ATOMIC;
+  a.out_mode = p->k_parts == 1 ? OUT_STORE : p->two_pass ? OUT_PARTIAL : OUT_ATOMIC;
   return a;
 }
 
@@ -305,8 +327,9 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   p->n_units = (int32_t)n_units;
   p->ch = choose(p, M);
   const size_t mn4 = (size_t)M * (size_t)N * 4;
+  p->two_pass = k_parts > 1 && two_pass_split(M, mn4 * (size_t)k_parts, out_dtype == QGEMM_F16, flags);
   if (k_parts == 1) p->ws_bytes = 0;
-  else if (flags & QGEMM_DETERMINISTIC) p->ws_bytes = mn4 * (size_t)k_parts;
+  else if (p->two_pass) p->ws_bytes = mn4 * (size_t)k_parts;
   else p->ws_bytes = out_dtype == QGEMM_F16 ? mn4 : 0;  // int32 output: atomics straight into C
   if (packed_bytes) *packed_bytes = p->L.total;
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
