@@ -63,6 +63,14 @@ SMALL = [
     (17, 136, 1024, "i2", 0, False),
     (32, 264, 2048, "i2", 0, False),
     (24, 520, 512, "i8", 0, False),
+    # the matrix-core GEMVs with two 16-column blocks per workgroup (N = 6000) and one
+    # (N = 4096 at k_parts 1)
+    (8, 6000, 512, "i8", 0, False),
+    (20, 6000, 1024, "i4", 128, False),
+    (4, 6000, 1024, "f16", 0, False),
+    (3, 6000, 2048, "i2", 0, False),
+    (30, 4096, 1024, "u4", 128, True),
+    (12, 4096, 1024, "i2", 0, False),
     # int8 / int2 rows 2..8 on the matrix cores (ragged last 64-column block)
     (2, 200, 1024, "i8", 0, False),
     (3, 72, 2048, "i2", 0, False),

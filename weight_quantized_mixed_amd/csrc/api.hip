@@ -16,6 +16,7 @@ struct qg_choice {
   int dl_tile;       // direct-load MFMA tile, or -1
   int tile;          // LDS-staged MFMA tile (used when dl_tile < 0)
   int gemv_waves;    // GEMV waves per workgroup
+  int gemv_cb;       // matrix-core GEMV: 16-column blocks per workgroup
   bool gemv_narrow;  // M = 1 with fewer than 128 blocks of 64 columns: 16-column workgroups
   bool gemv_mfma;    // int8 / int2 GEMV on the matrix cores
   bool gemv_mfma4;   // int4 / uint4 GEMV on the matrix cores (also for 8 < M <= 32)
@@ -112,8 +113,8 @@ bool choose_gemv_narrow(const qgemm_plan* p, int64_t M) {
   return M == 1 && (p->N + 63) / 64 * p->k_parts < QG_GEMV_NARROW_BELOW;
 }
 
-int choose_gemv_waves(const qgemm_plan* p, bool narrow) {
-  const int64_t rb = (p->N + (narrow ? 15 : 63)) / (narrow ? 16 : 64);
+int choose_gemv_waves(const qgemm_plan* p, int cols) {
+  const int64_t rb = (p->N + cols - 1) / cols;
   const int64_t per_part = p->L.nkb / p->k_parts;
   int64_t want = (QG_GEMV_TARGET_WAVES + rb * p->k_parts - 1) / (rb * p->k_parts);
   int64_t maxw = per_part / 2;
@@ -122,6 +123,19 @@ int choose_gemv_waves(const qgemm_plan* p, bool narrow) {
   if (want > maxw) want = maxw;
   if (want < 1) want = 1;
   return (int)want;
+}
+
+// 16-column blocks per workgroup of the matrix-core GEMVs: the most (4, sharing each
+// activation load) whose workgroups still occupy 60 % of the 256 CUs, else 1.  N =
+// 4096 thus runs 256 workgroups of 16 columns instead of 64 of 64: W4A16 M = 8,
+// K = 11008 in 10.0 against 16.4 us, fp16 M = 8, K = 4096 in 8.1 against 14.1 us.
+int choose_gemv_cb(const qgemm_plan* p) {
+  for (int cb : {4, 2}) {
+    const int64_t wgs = (p->N + 16 * cb - 1) / (16 * cb) * p->k_parts;
+    const int64_t waves = (wgs + 255) / 256;
+    if (wgs * 10 >= waves * 256 * 6) return cb;
+  }
+  return 1;
 }
 
 // LDS-staged kernel: largest tile that still gives every CU a workgroup (256 CUs).
@@ -181,7 +195,8 @@ qg_choice choose(const qgemm_plan* p, int64_t M) {
   c.gemv_mfma4 = (p->L.fmt == FMT_I4 || p->L.fmt == FMT_U4) && !c.gemv_narrow && smode != SC_PIECE &&
                  M >= QG_GEMV4_MFMA_MIN_M &&
                  M <= (smode == SC_NONE ? QG_GEMV4_MFMA_MAX_M_UNSCALED : QG_GEMV4_MFMA_MAX_M);
-  c.gemv_waves = choose_gemv_waves(p, c.gemv_narrow);
+  c.gemv_cb = (c.gemv_mfma || c.gemv_mfma4) ? choose_gemv_cb(p) : 4;
+  c.gemv_waves = choose_gemv_waves(p, c.gemv_narrow ? 16 : (c.gemv_mfma || c.gemv_mfma4) ? 16 * c.gemv_cb : 64);
   return c;
 }
 
@@ -215,6 +230,7 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
   a.unit_kb = p->unit_kb;
   a.n_units = p->n_units;
   a.waves = ch.gemv_waves;
+  a.gemv_cb = ch.gemv_cb;
   a.sb_per_group = p->group_size > KB ? p->group_size / KB : p->group_size < 0 ? (int32_t)p->L.nkb : 1;
   a.out_mode = p->k_parts == 1 ? OUT_STORE : p->two_pass ? OUT_PARTIAL : OUT_ATOMIC;
   return a;

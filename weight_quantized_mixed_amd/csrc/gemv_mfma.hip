@@ -72,7 +72,7 @@ __device__ __forceinline__ float4v mfma(const int4v& A, const int4v& B, const fl
 }
 
 // MB row blocks of 16 (M <= 16 MB)
-template <int FMT, int MB>
+template <int FMT, int MB, int CB>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs a) {
   constexpr bool I2 = FMT == FMT_I2, FP = FMT == FMT_F16;
   constexpr int KB = kb_of(FMT);   // positions per superblock: 256 (int2), 64 (int8), 32 (fp16)
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
   const int cnt = __builtin_amdgcn_readfirstlane(kb1 - kb0 > wave ? (kb1 - kb0 - wave + a.waves - 1) / a.waves : 0);
   auto row_of = [&](int j) { return __builtin_amdgcn_readfirstlane(kb0 + wave + j * a.waves); };
 
-  const uint4* __restrict__ Wl = a.W + (size_t)rb * 4 * 64 + lane;  // column block rb*4 + cb at + cb*64
+  const uint4* __restrict__ Wl = a.W + (size_t)rb * CB * 64 + lane;  // column block rb*CB + cb at + cb*64
   const uint32_t sb_stride = (uint32_t)a.NB * 64u;                   // uint4 per superblock row
   // this lane's activation slice: row r16, K group g of each superblock.  Lanes of
   // rows past M read row M - 1 (results dropped): the loads stay unconditional,
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
   // never waits for the weight loads of the stage after it
   struct Stage {
     uint4 av[MB][AV];
-    uint4 w[4];
+    uint4 w[CB];
   };
   auto load = [&](Stage& s, int j) {
     const uint32_t kb = (uint32_t)row_of(min(j, cnt - 1));
@@ -123,16 +123,16 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
 #pragma unroll
       for (int i = 0; i < AV; ++i) s.av[r][i] = load16(Al[r] + kb * (KB * ESZ / 16) + i);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) s.w[cb] = stream_load(Wl + kb * sb_stride + cb * 64);
+    for (int cb = 0; cb < CB; ++cb) s.w[cb] = stream_load(Wl + kb * sb_stride + cb * 64);
   };
 
-  acc_v acc[MB][4][NC];
+  acc_v acc[MB][CB][NC];
   int4v accS[MB];  // int2: activation sums of classes 0-2
 #pragma unroll
   for (int r = 0; r < MB; ++r) {
     accS[r] = int4v{0, 0, 0, 0};
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[r][cb][c] = acc_v{0, 0, 0, 0};
   }
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
         A[3] = int4v{mv(s.av[r][0].w), mv(s.av[r][1].w), mv(s.av[r][2].w), mv(s.av[r][3].w)};
         if constexpr (NC == 4) {
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
+          for (int cb = 0; cb < CB; ++cb) {
             const uint4 w = s.w[cb];
             acc[r][cb][0] = mfma(A[0], masked(w, 0x03030303u), acc[r][cb][0]);
             acc[r][cb][1] = mfma(A[1], masked(w, 0x0C0C0C0Cu), acc[r][cb][1]);
@@ -159,15 +159,15 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
           }
         } else {
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[r][cb][0] = mfma(A[0], masked(s.w[cb], 0x03030303u), acc[r][cb][0]);
+          for (int cb = 0; cb < CB; ++cb) acc[r][cb][0] = mfma(A[0], masked(s.w[cb], 0x03030303u), acc[r][cb][0]);
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
+          for (int cb = 0; cb < CB; ++cb)
             acc[r][cb][0] = mfma(A[1], shifted_masked(s.w[cb], 2, 0x03030303u), acc[r][cb][0]);
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
+          for (int cb = 0; cb < CB; ++cb)
             acc[r][cb][0] = mfma(A[2], shifted_masked(s.w[cb], 4, 0x03030303u), acc[r][cb][0]);
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[r][cb][1] = mfma(A[3], masked(s.w[cb], 0xC0C0C0C0u), acc[r][cb][1]);
+          for (int cb = 0; cb < CB; ++cb) acc[r][cb][1] = mfma(A[3], masked(s.w[cb], 0xC0C0C0C0u), acc[r][cb][1]);
         }
         const int4v ones = int4v{0x01010101, 0x01010101, 0x01010101, 0x01010101};
         accS[r] = mfma(A[0], ones, accS[r]);
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
         accS[r] = mfma(A[2], ones, accS[r]);
       } else {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[r][cb][0] = mfma(as_i4(s.av[r][0]), as_i4(s.w[cb]), acc[r][cb][0]);
+        for (int cb = 0; cb < CB; ++cb) acc[r][cb][0] = mfma(as_i4(s.av[r][0]), as_i4(s.w[cb]), acc[r][cb][0]);
       }
     }
   };
@@ -212,11 +212,11 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
 
   // lane l holds rows 16 rb + 4 (l / 16) + i of column l % 16 of each column block;
   // the waves meet in LDS
-  __shared__ acc_t red[GEMV_MAX_WAVES][MB][4][4][64];
+  __shared__ acc_t red[GEMV_MAX_WAVES][MB][CB][4][64];
 #pragma unroll
   for (int r = 0; r < MB; ++r)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc_t v = acc[r][cb][0][i];
@@ -227,9 +227,9 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
         red[wave][r][cb][i][lane] = v;
       }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < MB * 4 * 4 * 64; idx += blockDim.x) {
-    const int r = idx >> 10, cb = (idx >> 8) & 3, i = (idx >> 6) & 3, ln = idx & 63;
-    const int row = r * 16 + 4 * (ln >> 4) + i, col = rb * 64 + cb * 16 + (ln & 15);
+  for (int idx = threadIdx.x; idx < MB * CB * 4 * 64; idx += blockDim.x) {
+    const int r = idx / (CB * 256), cb = (idx >> 8) % CB, i = (idx >> 6) & 3, ln = idx & 63;
+    const int row = r * 16 + 4 * (ln >> 4) + i, col = (rb * CB + cb) * 16 + (ln & 15);
     if (row >= a.M || col >= a.N) continue;
     acc_t s = 0;
     for (int w = 0; w < a.waves; ++w) s += red[w][r][cb][i][ln];
@@ -251,25 +251,32 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma_kernel(RunArgs 
   }
 }
 
+template <int FMT, int MB, int CB>
+void launch_cb(const RunArgs& a, hipStream_t st) {
+  const dim3 grid((a.N + 16 * CB - 1) / (16 * CB), a.k_parts), block(64 * a.waves);
+  hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MB, CB>), grid, block, 0, st, a);
+}
+
+template <int FMT, int MB>
+hipError_t launch_mb(const RunArgs& a, hipStream_t st) {
+  switch (a.gemv_cb) {
+    case 1: launch_cb<FMT, MB, 1>(a, st); break;
+    case 2: launch_cb<FMT, MB, 2>(a, st); break;
+    case 4: launch_cb<FMT, MB, 4>(a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemv_mfma(int fmt, const RunArgs& a, hipStream_t st) {
   if (a.M < 1 || a.M > 32) return hipErrorInvalidValue;
-  const dim3 grid((a.N + 63) / 64, a.k_parts), block(64 * a.waves);
   const bool two = a.M > 16;
-  if (fmt == FMT_I8) {
-    if (two) hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I8, 2>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I8, 1>), grid, block, 0, st, a);
-  } else if (fmt == FMT_I2) {
-    if (two) hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I2, 2>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((gemv_mfma_kernel<FMT_I2, 1>), grid, block, 0, st, a);
-  } else if (fmt == FMT_F16) {
-    if (two) hipLaunchKernelGGL((gemv_mfma_kernel<FMT_F16, 2>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((gemv_mfma_kernel<FMT_F16, 1>), grid, block, 0, st, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (fmt == FMT_I8) return two ? launch_mb<FMT_I8, 2>(a, st) : launch_mb<FMT_I8, 1>(a, st);
+  if (fmt == FMT_I2) return two ? launch_mb<FMT_I2, 2>(a, st) : launch_mb<FMT_I2, 1>(a, st);
+  if (fmt == FMT_F16) return two ? launch_mb<FMT_F16, 2>(a, st) : launch_mb<FMT_F16, 1>(a, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qg

@@ -69,7 +69,7 @@ __device__ __forceinline__ float4v mfma(const uint4& A, const uint4& B, const fl
 }
 
 // VAR: 0 unscaled, 1 scaled, 2 scaled with zero points
-template <int FMT, int MB, int VAR>
+template <int FMT, int MB, int VAR, int CB>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs a) {
   constexpr int KB = 128, NS = 4;  // positions and 32-position MFMA steps per superblock
   constexpr bool SCALED = VAR >= 1, ZEROS = VAR == 2;
@@ -93,12 +93,12 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
     Al[r] = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.A) + (size_t)min(r * 16 + n16, a.M - 1) * a.K) + g;
 
   // piece l of each superblock (16 bytes) for lane l, as stored
-  const uint4* __restrict__ Wq = a.W + (size_t)rb * 4 * 64 + lane;
+  const uint4* __restrict__ Wq = a.W + (size_t)rb * CB * 64 + lane;
   const uint32_t sbq_stride = (uint32_t)a.NB * 64u;  // uint4 per superblock row
   struct Stage {
     uint4 av[MB][NS];  // A operand of each row block and step
-    uint4 wq[4];        // piece (lane / 16, lane % 16) of each column block, as stored
-    uint32_t sc[4];     // raw scale (| zero << 16) of each column block
+    uint4 wq[CB];       // piece (lane / 16, lane % 16) of each column block, as stored
+    uint32_t sc[CB];    // raw scale (| zero << 16) of each column block
   };
   auto load = [&](Stage& s, int j) {
     const uint32_t kb = (uint32_t)row_of(min(j, cnt - 1));
@@ -107,46 +107,46 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
 #pragma unroll
       for (int t = 0; t < NS; ++t) s.av[r][t] = load16(Al[r] + kb * (KB / 8) + t * 4);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) s.wq[cb] = stream_load16(Wq + kb * sbq_stride + cb * 64);
+    for (int cb = 0; cb < CB; ++cb) s.wq[cb] = stream_load16(Wq + kb * sbq_stride + cb * 64);
     if constexpr (SCALED) {
       const uint32_t grp = a.sb_per_group == 1 ? kb : kb / (uint32_t)a.sb_per_group;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const uint32_t col = (uint32_t)(rb * 64 + cb * 16 + n16);
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t col = (uint32_t)((rb * CB + cb) * 16 + n16);
         if constexpr (ZEROS) s.sc[cb] = static_cast<const uint32_t*>(a.S)[grp * (uint32_t)a.Npad + col];
         else s.sc[cb] = static_cast<const uint16_t*>(a.S)[grp * (uint32_t)a.Npad + col];
       }
     }
   };
 
-  float4v acc[MB][4];
+  float4v acc[MB][CB];
 #pragma unroll
   for (int r = 0; r < MB; ++r)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[r][cb] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) acc[r][cb] = float4v{0.f, 0.f, 0.f, 0.f};
 
   const uint4 ONES = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
   auto consume = [&](const Stage& s) {
     // packed word of each column block and step: word g of the piece of step t
-    uint32_t w[4][NS];
+    uint32_t w[CB][NS];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       uint32_t x[4] = {s.wq[cb].x, s.wq[cb].y, s.wq[cb].z, s.wq[cb].w};
       transpose_rows(x);
 #pragma unroll
       for (int t = 0; t < NS; ++t) w[cb][t] = x[t];
     }
-    float4v T[MB][4], S[MB];
+    float4v T[MB][CB], S[MB];
 #pragma unroll
     for (int r = 0; r < MB; ++r) {
       S[r] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) T[r][cb] = float4v{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < CB; ++cb) T[r][cb] = float4v{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         const uint32_t wd = w[cb][t];
         const uint4 B = make_uint4(and_or(wd, 0x000F000Fu, 0x64006400u), and_or(wd >> 4, 0x000F000Fu, 0x64006400u),
                                    and_or(wd >> 8, 0x000F000Fu, 0x64006400u), and_or(wd >> 12, 0x000F000Fu, 0x64006400u));
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
       for (int r = 0; r < MB; ++r) S[r] = mfma(s.av[r][t], ONES, S[r]);
     }
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       float sc = 1.f, c = BIAS;
       if constexpr (SCALED) sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(s.sc[cb] & 0xFFFFu));
       if constexpr (ZEROS) c += (float)__builtin_bit_cast(_Float16, (uint16_t)(s.sc[cb] >> 16));
@@ -197,17 +197,17 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
 
   // lane l holds rows 16 r + 4 (l / 16) + i of column l % 16 of each column block;
   // the waves meet in LDS
-  __shared__ float red[GEMV_MAX_WAVES][MB][4][4][64];
+  __shared__ float red[GEMV_MAX_WAVES][MB][CB][4][64];
 #pragma unroll
   for (int r = 0; r < MB; ++r)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][r][cb][i][lane] = acc[r][cb][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < MB * 4 * 4 * 64; idx += blockDim.x) {
-    const int r = idx >> 10, cb = (idx >> 8) & 3, i = (idx >> 6) & 3, ln = idx & 63;
-    const int row = r * 16 + 4 * (ln >> 4) + i, col = rb * 64 + cb * 16 + (ln & 15);
+  for (int idx = threadIdx.x; idx < MB * CB * 4 * 64; idx += blockDim.x) {
+    const int r = idx / (CB * 256), cb = (idx >> 8) % CB, i = (idx >> 6) & 3, ln = idx & 63;
+    const int row = r * 16 + 4 * (ln >> 4) + i, col = (rb * CB + cb) * 16 + (ln & 15);
     if (row >= a.M || col >= a.N) continue;
     float v = 0.f;
     for (int w = 0; w < a.waves; ++w) v += red[w][r][cb][i][ln];
@@ -218,15 +218,25 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
   }
 }
 
-template <int FMT, int MB>
-hipError_t launch_mb(const RunArgs& a, hipStream_t st) {
-  const dim3 grid((a.N + 63) / 64, a.k_parts), block(64 * a.waves);
+template <int FMT, int MB, int CB>
+hipError_t launch_cb(const RunArgs& a, hipStream_t st) {
+  const dim3 grid((a.N + 16 * CB - 1) / (16 * CB), a.k_parts), block(64 * a.waves);
   const int var = a.smode == SC_NONE ? 0 : a.zeros ? 2 : 1;
-  if (var == 0) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT, MB, 0>), grid, block, 0, st, a);
-  else if (var == 1) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT, MB, 1>), grid, block, 0, st, a);
-  else if (FMT == FMT_U4) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT_U4, MB, 2>), grid, block, 0, st, a);
+  if (var == 0) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT, MB, 0, CB>), grid, block, 0, st, a);
+  else if (var == 1) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT, MB, 1, CB>), grid, block, 0, st, a);
+  else if (FMT == FMT_U4) hipLaunchKernelGGL((gemv_mfma4_kernel<FMT_U4, MB, 2, CB>), grid, block, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <int FMT, int MB>
+hipError_t launch_mb(const RunArgs& a, hipStream_t st) {
+  switch (a.gemv_cb) {
+    case 1: return launch_cb<FMT, MB, 1>(a, st);
+    case 2: return launch_cb<FMT, MB, 2>(a, st);
+    case 4: return launch_cb<FMT, MB, 4>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

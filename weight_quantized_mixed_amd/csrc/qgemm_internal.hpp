@@ -81,6 +81,7 @@ struct RunArgs {
   int32_t waves;        // GEMV: waves per workgroup (K split inside the workgroup)
   int32_t sb_per_group; // superblocks per scale group (nkb when one group spans K)
   int32_t g_shift;      // group of position p = p >> g_shift, or -1: p / group_size
+  int32_t gemv_cb;      // matrix-core GEMV: 16-column blocks per workgroup (1, 2 or 4)
   const void* bias;     // [N] of the output type, or null
   // int8 activations with fp16 output: C = fp16(acc * row_scale[m] * col_scale[n]
   // (+ bias)); null for int32 output
