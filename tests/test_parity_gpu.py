@@ -71,6 +71,10 @@ SMALL = [
     (3, 6000, 2048, "i2", 0, False),
     (30, 4096, 1024, "u4", 128, True),
     (12, 4096, 1024, "i2", 0, False),
+    # two int4 rows on the matrix cores when N is narrow
+    (2, 4096, 1024, "i4", 128, False),
+    (2, 520, 1024, "u4", 128, True),
+    (2, 1000, 512, "i4", 0, False),
     # int8 / int2 rows 2..8 on the matrix cores (ragged last 64-column block)
     (2, 200, 1024, "i8", 0, False),
     (3, 72, 2048, "i2", 0, False),

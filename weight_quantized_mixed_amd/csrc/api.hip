@@ -192,9 +192,12 @@ qg_choice choose(const qgemm_plan* p, int64_t M) {
   c.gemv_mfma = !c.gemv_narrow && M >= QG_GEMV_MFMA_MIN_M && M <= QG_GEMV_MFMA_MAX_M &&
                 ((QG_GEMV_MFMA_FMTS >> p->L.fmt) & 1);
   const int smode = scale_mode(p->L.fmt, p->group_size);
+  // two rows as well when the matrix is narrow enough for 16- or 32-column
+  // workgroups, which the dot-product GEMV does not have (N = 4096: 4.8 against
+  // 7.8 us at K = 4096, 8.4 against 16.0 us at K = 11008)
+  const int min_m4 = choose_gemv_cb(p) < 4 ? 2 : QG_GEMV4_MFMA_MIN_M;
   c.gemv_mfma4 = (p->L.fmt == FMT_I4 || p->L.fmt == FMT_U4) && !c.gemv_narrow && smode != SC_PIECE &&
-                 M >= QG_GEMV4_MFMA_MIN_M &&
-                 M <= (smode == SC_NONE ? QG_GEMV4_MFMA_MAX_M_UNSCALED : QG_GEMV4_MFMA_MAX_M);
+                 M >= min_m4 && M <= (smode == SC_NONE ? QG_GEMV4_MFMA_MAX_M_UNSCALED : QG_GEMV4_MFMA_MAX_M);
   c.gemv_cb = (c.gemv_mfma || c.gemv_mfma4) ? choose_gemv_cb(p) : 4;
   c.gemv_waves = choose_gemv_waves(p, c.gemv_narrow ? 16 : (c.gemv_mfma || c.gemv_mfma4) ? 16 * c.gemv_cb : 64);
   return c;
