@@ -241,10 +241,11 @@ def test_atomic_split_past_the_partials_cap(w_dtype, g, zeros):
 # workgroups (N / BN x M / BM x k_parts) still occupies 60 % of the 256 CUs; up to 32
 # rows every format takes a matrix-core GEMV instead.  These shapes select, in order:
 # 32x64, 32x128 (33..64 rows and few columns), 64x128, 64x256, 128x256, 256x256,
-# 128x128 (int4 / uint4 / int2; 64x256 for the others), and the skinny matrix-core
-# GEMV with k_parts 4 (rows and columns ragged).
+# 128x128 (int4 / uint4 / int2; 64x256 for the others), the skinny matrix-core GEMV
+# with k_parts 4, and 128x256 at 400 rows (rows and columns ragged).
 DL_SHAPES = [(40, 1000, 1, False), (40, 12000, 1, False), (40, 16376, 2, False), (40, 16376, 4, True),
-             (100, 16376, 4, False), (300, 16376, 2, True), (100, 24000, 1, False), (20, 16376, 4, False)]
+             (100, 16376, 4, False), (300, 16376, 2, True), (100, 24000, 1, False), (20, 16376, 4, False),
+             (400, 16376, 1, False)]
 DL_FORMATS = [("i4", 128, False), ("u4", 128, True), ("u4", 256, False), ("i4", 0, False), ("f16", 0, False),
               ("i8", 0, False), ("i2", 0, False)]
 
