@@ -4,9 +4,10 @@
 // a gfx950 16x16 MFMA B operand (lane l: column l % 16, K group l / 16), so one
 // wave-wide 16-byte load of a superblock is an MFMA operand as it stands
 // (int8), or four of them after masking (int2): no LDS, no transposition.  A
-// workgroup owns 64 columns (four superblock columns) and a k-part; its waves
-// take the part's superblock rows in turn (as the VALU GEMV does) and meet in
-// LDS at the end.  The activation rows ride in the A operand: lane l loads the
+// workgroup owns CB superblock columns (16, 32 or 64 columns: the most that
+// still gives the CUs enough workgroups; each activation load then serves CB
+// MFMAs) and a k-part; its waves take the part's superblock rows in turn (as the
+// VALU GEMV does) and meet in LDS at the end.  The activation rows ride in the A operand: lane l loads the
 // K group l / 16 of row l % 16 (rows past M repeat row M - 1, and their results
 // are dropped), so up to 16 rows cost the same instructions as one; a second row
 // block of 16 reuses every B operand.

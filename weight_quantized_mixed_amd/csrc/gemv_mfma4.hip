@@ -14,6 +14,10 @@
 // (lane l: row l % 16 of the row block, positions 32 s + 8 g .. + 7), so one set
 // of B operands serves up to 16 rows per MFMA, two row blocks up to 32.
 //
+// A workgroup owns CB superblock columns (16, 32 or 64 columns, the most that still
+// gives the CUs enough workgroups) and a k-part; its waves take the part's
+// superblock rows in turn and meet in LDS at the end.
+//
 // Per superblock and column block the MFMAs accumulate T = sum a (1024 + b + q),
 // with b the offset of the code (8 for signed int4, 0 for uint4), into a
 // temporary; three more MFMAs per superblock against a B of fp16 ones give the
