@@ -334,6 +334,7 @@ def main():
     ap.add_argument("--no-grid", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="substring filter on grid entries")
+    ap.add_argument("--exact", action="store_true", help="--only names one grid entry exactly")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales HBM counters)")
     args = ap.parse_args()
@@ -388,7 +389,7 @@ def main():
     if not args.no_grid:
         grid = []
         for i, c in enumerate(GRID):
-            if args.only and args.only not in label(c):
+            if args.only and (label(c) != args.only if args.exact else args.only not in label(c)):
                 continue
             b = make_bench(c, synth.seed_for(6, i))
             grid.append(measure_grid_entry(b))
