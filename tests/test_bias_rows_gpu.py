@@ -22,14 +22,15 @@ BIAS_CASES = [
     # M, N, K, w_dtype, g, zeros, k_parts, deterministic
     (1, 300, 1024, "i4", 128, False, 1, False),    # GEMV, stored
     (1, 72, 512, "u4", 128, True, 1, False),       # 16-column GEMV
-    (3, 136, 1024, "u4", 64, True, 3, False),      # GEMV, fp32 atomics + finalize
+    (3, 136, 1024, "u4", 64, True, 3, False),      # GEMV, ordered partials + finalize
     (5, 200, 1024, "i8", 0, False, 3, False),      # GEMV, int32 atomics onto the bias rows
     (5, 200, 2048, "i2", 0, False, 2, True),       # GEMV, two-pass
     (40, 264, 1024, "i4", 128, False, 1, False),   # direct-load MFMA, stored
+    (20, 264, 1024, "i8", 0, False, 3, False),     # matrix-core GEMV, int32 atomics onto the bias rows
     (64, 72, 1024, "u4", 32, True, 1, False),      # LDS-staged MFMA (per-piece groups)
     (130, 264, 768, "i4", 64, False, 3, True),     # LDS-staged MFMA, two-pass
-    (129, 136, 512, "i8", 0, False, 3, False),     # direct-load, int32 atomics
-    (300, 520, 512, "f16", 0, False, 2, False),    # direct-load, fp32 atomics
+    (129, 136, 512, "i8", 0, False, 3, False),     # direct-load, int32 partials (128 rows and more)
+    (300, 520, 512, "f16", 0, False, 2, False),    # direct-load, ordered partials
     (160, 264, 1024, "i2", 0, False, 1, False),    # direct-load int, stored
 ]
 
@@ -40,6 +41,22 @@ def test_bias_epilogue(M, N, K, w_dtype, g, zeros, kp, det):
     c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=5000 + M + N)
     b = _bias(c, 5001 + N)
     assert_matches(c.run(bias=b), c.reference(bias=b), f"bias M={M} {w_dtype} kp={kp}")
+
+
+# split-K whose partials would pass 256 MiB keeps the atomic reductions: fp32 into the
+# zero-filled workspace (bias added by the finalize pass) and int32 onto the bias rows
+@pytest.mark.parametrize("w_dtype,g", [("i4", 128), ("i8", 0)])
+def test_bias_with_atomic_split(w_dtype, g):
+    M, N, K = 4100, 8400, 256
+    say(f"case bias atomic split M={M} N={N} K={K} {w_dtype} kp=2")
+    c = Case(M, N, K, w_dtype, g, False, k_parts=2, seed=5100)
+    assert c.q.ws_bytes == (M * N * 4 if w_dtype == "i4" else 0)
+    b = _bias(c, 5101)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([rng.choice(M, 150, replace=False), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(N, 150, replace=False), [0, N - 1]]))
+    gpu = c.run(bias=b)
+    assert_matches(gpu[np.ix_(rows, cols)], c.reference(rows=rows, cols=cols, bias=b), f"bias atomic {w_dtype}")
 
 
 ROW_PLANS = [
