@@ -54,11 +54,33 @@ def label(c):
         s += " zeros"
     if c.get("kp", 1) > 1:
         s += f" kp={c['kp']}"
+        # split-K reduction: atomics unless the entry names another
+        s += {"atomic": "", "det": " two-pass", "auto": " auto"}[c.get("split", "atomic")]
     if c.get("dq"):
         s += " dequant-fp16"
     if c.get("bias"):
         s += " bias"
     return s
+
+
+def make_qgemm(c):
+    """The plan a grid entry times (shared with the parity test of the grid)."""
+    from weight_quantized_mixed_amd.device import QGemm
+    g = c.get("g", 0) if c["w"] in ("i4", "u4") else 0
+    split = c.get("split", "atomic")
+    return QGemm(c["M"], c["N"], c["K"], c["w"], g, c.get("zeros", False), c.get("kp", 1),
+                 deterministic=split == "det", split_auto=split == "auto",
+                 dequant_output=bool(c.get("dq")))
+
+
+def run_entry(q, c, A, W, C, ws, bias=None, rs=None, cs=None):
+    """One call of a grid entry's plan, through the entry point the bench times."""
+    if c.get("dq"):
+        q.run_scaled(A, W, rs, cs, bias, C, ws)
+    elif bias is not None:
+        q.run(A, W, C, ws, bias=bias)
+    else:
+        q.run(A, W, C, ws)
 
 
 _WEIGHTS = {}
@@ -86,14 +108,14 @@ class Bench:
     def __init__(self, c, seed):
         import torch
         import synth
-        from weight_quantized_mixed_amd.device import QGemm, host_to_device
+        from weight_quantized_mixed_amd.device import host_to_device
         self.c = c
         M, N, K, wd = c["M"], c["N"], c["K"], c["w"]
-        g, z, kp = c.get("g", 0), c.get("zeros", False), c.get("kp", 1)
+        g, z = c.get("g", 0), c.get("zeros", False)
         if wd not in ("i4", "u4"):
             g = 0
         self.dq, bias = bool(c.get("dq")), bool(c.get("bias"))
-        self.q = QGemm(M, N, K, wd, g, z, kp, dequant_output=self.dq)
+        self.q = make_qgemm(c)
         self.packed = _weights(c, self.q, seed)
         A = host_to_device(synth.draw_activations(M, K, self.q.a_dtype, seed + M))
         n_a = 1 if A.numel() * A.element_size() >= 2 * MALL_BYTES else len(self.packed)
@@ -115,12 +137,8 @@ class Bench:
         j = self.i
         self.i += 1
         A, W = self.As[j % len(self.As)], self.packed[j % len(self.packed)]
-        if self.dq:
-            self.q.run_scaled(A, W, self.rs, self.cs, self.bias, self.C, self.ws)
-        elif self.bias is not None:
-            self.q.run(A, W, self.C, self.ws, bias=self.bias)
-        else:
-            self.q.run(A, W, self.C, self.ws)
+        run_entry(self.q, self.c, A, W, self.C, self.ws, self.bias,
+                  self.rs if self.dq else None, self.cs if self.dq else None)
 
     def timed(self, n):
         """Seconds per call over n back-to-back calls (HIP events on the launch stream)."""
@@ -247,22 +265,28 @@ def measure_grid_entry(b, bursts=50):
     del g
     t = statistics.median(samples)
     bound, frac = b.roof(t)
-    return {"config": label(b.c), "us": round(t * 1e6, 3),
-            "p10_us": round(samples[max(0, len(samples) // 10)] * 1e6, 3),
-            "p90_us": round(samples[min(len(samples) - 1, (9 * len(samples)) // 10)] * 1e6, 3),
-            ("TFLOPS" if b.a_kind == "f16" else "TOPS"): round(b.flops / t / 1e12, 3),
-            "GBps": round(b.bytes / t / 1e9, 1), "bound": bound, "roofline_frac": round(frac, 4),
+    # compact keys: the JSON line carries every entry of the grid
+    return {"c": label(b.c), "us": round(t * 1e6, 2),
+            "p10": round(samples[max(0, len(samples) // 10)] * 1e6, 2),
+            "p90": round(samples[min(len(samples) - 1, (9 * len(samples)) // 10)] * 1e6, 2),
+            ("tflops" if b.a_kind == "f16" else "tops"): round(b.flops / t / 1e12, 2),
+            "gbs": round(b.bytes / t / 1e9), "bound": bound, "frac": round(frac, 3),
             "path": b.path_name}
 
 
 GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128, 512)]
-        + [{"w": "i4", "M": 1, "N": 16384, "K": 16384, "g": 128, "kp": 4}]
+        + [{"w": "i4", "M": 1, "N": 16384, "K": 16384, "g": 128, "kp": 4, "split": sp}
+           for sp in ("atomic", "det")]
         + [{"w": w, "M": M, "N": 16384, "K": 16384, "kp": kp} for w in ("i8", "i2")
            for M in (1, 32, 128, 512) for kp in (1, 4)]
+        + [{"w": w, "M": M, "N": 16384, "K": 16384, "kp": 4, "split": "auto"} for w in ("i8", "i2")
+           for M in (128, 512)]
         + [{"w": "f16", "M": M, "N": 16384, "K": 16384} for M in (1, 32, 128, 512)]
-        + [{"w": "i4", "M": M, "N": N, "K": K, "g": 128, "kp": kp} for M in (1, 128)
-           for (K, N) in ((4096, 11008), (11008, 4096), (4096, 4096), (4096, 32000)) for kp in (1, 4)]
-        + [{"w": "i4", "M": 1, "N": 4096, "K": 4096, "g": 128}]
+        # the LLaMA-7B projection shapes with k-parts 1 and 4: atomic fp32 reduction (the
+        # pages' parallel-k) and the ordered two-pass one
+        + [{"w": "i4", "M": M, "N": N, "K": K, "g": 128, "kp": kp, "split": sp} for M in (1, 128)
+           for (K, N) in ((4096, 11008), (11008, 4096), (4096, 4096), (4096, 32000))
+           for (kp, sp) in ((1, "atomic"), (4, "atomic"), (4, "det"))]
         + [{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": g} for g in (0, -1) for M in (1, 32, 128, 512)]
         # bias epilogue; int8 products with the dequantised fp16 output; the per-row
         # int8 quantiser of fp16 activations
@@ -272,6 +296,10 @@ GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128
         + [{"w": "quant", "M": M, "K": 16384} for M in (512, 16384)]
         + [{"w": "f16", "M": 16384, "N": 16384, "K": 16384},
            {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}])
+
+
+# the timed workload: W4A16 decode at M = 1, N = K = 16384, g = 128, k_parts = 1
+HEADLINE = {"w": "i4", "M": 1, "N": 16384, "K": 16384, "g": 128}
 
 
 def make_bench(c, seed):
@@ -324,6 +352,24 @@ def cpu_baseline(c, seed):
             "seconds": round(dt, 3), "host_cpus": os.cpu_count()}
 
 
+# the rows that carry a stated target: >= 70 % of the HBM roofline for W4A16 and W2A8
+# at M = 1, >= 60 % of the dense fp16 MFMA peak at M = N = K = 16384
+TARGET_ROWS = {"w2a8_m1": ("i2 M=1 N=16384 K=16384", 0.70),
+               "f16_16384": ("f16 M=16384 N=16384 K=16384", 0.60),
+               "u4z_16384": ("u4 M=16384 N=16384 K=16384 g=128 zeros", 0.60)}
+
+
+def targets(out):
+    """µs and roofline fraction of each targeted row (last on the line, so that a
+    reader of the line's tail sees them)."""
+    t = {"w4a16_m1": {"us": out["config"]["us_per_call"], "frac": out["roofline"]["frac"], "goal": 0.70}}
+    rows = {r["c"]: r for r in out.get("grid", [])}
+    for key, (lab, goal) in TARGET_ROWS.items():
+        if lab in rows:
+            t[key] = {"us": rows[lab]["us"], "frac": rows[lab]["frac"], "goal": goal}
+    return t
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,7 +405,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}))
         return
 
-    head = {"w": "i4", "M": 1, "N": 16384, "K": 16384, "g": 128}
+    head = HEADLINE
     print(f"[bench] workload {label(head)}", file=sys.stderr, flush=True)
     hb = Bench(head, synth.seed_for(5))
     hb.timed_bound(args.warmup)
@@ -393,14 +439,16 @@ def main():
                 continue
             b = make_bench(c, synth.seed_for(6, i))
             grid.append(measure_grid_entry(b))
-            print(f"[bench] {grid[-1]}", file=sys.stderr, flush=True)
+            r = grid[-1]
+            print(f"[bench] {r['c']}: {r['us']} us, {r['frac']}", file=sys.stderr, flush=True)
             b.close()
             del b
             time.sleep(0.05)   # gap between configurations
         out["grid"] = grid
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(head, synth.seed_for(5))
-    print(json.dumps(out), flush=True)
+    out["targets"] = targets(out)
+    print(json.dumps(out, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":

@@ -81,8 +81,13 @@ typedef enum {
   QGEMM_I2 = 7  /* signed int2, [-2, 1] */
 } qgemm_dtype;
 
-/* flags for qgemm_create */
-#define QGEMM_DETERMINISTIC 1u /* k_parts > 1: fixed-order two-pass reduction instead of atomics */
+/* flags for qgemm_create (k_parts > 1 only; without flags the parts are reduced
+   with global atomics, the parallel-k reduction of hidet issue #364) */
+#define QGEMM_DETERMINISTIC 1u /* fixed-order two-pass reduction: bitwise reproducible */
+#define QGEMM_SPLIT_AUTO 2u    /* the reduction that measured faster for the plan's shape:
+                                  two-pass for fp16 outputs and for int32 outputs from 128
+                                  rows while the partials stay within 256 MiB, else atomics;
+                                  QGEMM_DETERMINISTIC takes precedence */
 
 /* execution path chosen by a plan (qgemm_plan_path) */
 #define QGEMM_PATH_GEMV 1 /* M <= 8: skinny kernels streaming the weights once (dot products at
@@ -91,7 +96,10 @@ typedef enum {
                              LDS-staged tiles) */
 
 /*
- * Create a plan.  No device call.
+ * Create a plan: the problem statement of BitBLAS issue #252's Matmul
+ * configuration (M, N, K, A_dtype, W_dtype, out_dtype, accum_dtype, group_size,
+ * with_scaling as group_size != 0, with_zeros) plus hidet issue #364's k-parts.
+ * No device call.
  *   M, N, K       problem sizes, each >= 1.  K must be a multiple of the block
  *                 depth of the weight format: 128 (I4/U4), 256 (I2), 64 (I8),
  *                 32 (F16), else QGEMM_ERR_UNSUPPORTED.
@@ -102,11 +110,11 @@ typedef enum {
  *   has_zeros     0 or 1; 1 only with w_dtype U4 and group_size != 0.
  *   k_parts       >= 1: number of contiguous, group-aligned K ranges computed by
  *                 separate workgroups and reduced with fp32/int32 global atomics
- *                 or by ordered partials and one summing pass (always with
- *                 QGEMM_DETERMINISTIC; see qgemm_run).  At most K / unit, where
+ *                 (default) or by ordered partials and one summing pass
+ *                 (QGEMM_DETERMINISTIC; see qgemm_run).  At most K / unit, where
  *                 unit = group_size when it is a multiple of the block depth
  *                 (and larger), else the block depth.
- *   flags         0 or QGEMM_DETERMINISTIC.
+ *   flags         0, or QGEMM_DETERMINISTIC and / or QGEMM_SPLIT_AUTO.
  *   packed_bytes  out: size of the packed blob for qgemm_pack_weights/qgemm_run.
  *   workspace_bytes out: size of the device workspace qgemm_run needs (0 if none).
  */
@@ -117,7 +125,9 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K,
                           size_t* workspace_bytes);
 
 /*
- * Pack canonical weights (device memory, layout above) into the plan's blob.
+ * Pack canonical weights (device memory, layout above) into the plan's blob: the
+ * backend-specific pre-shuffled weight of torchao issue #2752's "dtype +
+ * packing_format" tensors, built from BitBLAS issue #252's "nt" weight layout.
  *   w       device, canonical weights.
  *   scales  device, fp16 [N, G]; required iff group_size != 0, else ignored.
  *   zeros   device, fp16 [N, G]; required iff has_zeros, else ignored.
@@ -128,18 +138,24 @@ qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const voi
                                 const void* zeros, void* packed, void* stream);
 
 /*
- * C = A . dequant(W) on `stream`.
+ * C = A . dequant(W) on `stream` (the quantized matmul of hidet issue #364 and
+ * BitBLAS issue #252; int8 x int8 / int2 products accumulate and return int32,
+ * Triton PR #3595).
  *   A          device, [M, K] fp16 or int8, 16-byte aligned.
  *   packed     device, the blob written by qgemm_pack_weights.
  *   C          device, [M, N] fp16 or int32; fully overwritten.
  *   workspace  device, >= workspace_bytes (may be NULL when that is 0),
- *              16-byte aligned; scratch for split-K partials, its contents on
- *              entry are ignored.
- * Split-K sums the parts in an order the library chooses per plan (ordered
- * partials for fp16 outputs and for 128 rows or more whenever their workspace
- * stays within 256 MiB, else atomics): results with atomics may differ in the
- * last fp16 bits between runs, int32 results are exact either way.  With
- * QGEMM_DETERMINISTIC the result is always bitwise reproducible.
+ *              16-byte aligned; scratch for split-K, its contents on entry are
+ *              ignored.
+ * Split-K (k_parts > 1) reduces the parts with global atomics unless a flag says
+ * otherwise: fp16 outputs add fp32 partials into the zero-filled workspace
+ * (M * N * 4 bytes), which one more pass rounds into C; int32 outputs add
+ * straight into C (no workspace).  fp32 atomics add in the order the parts
+ * finish, so fp16 results may differ in the last bits between runs (each within
+ * the accuracy of the fp32 sum); int32 results are exact and identical.  With
+ * QGEMM_DETERMINISTIC (and with QGEMM_SPLIT_AUTO where it picks them) the parts
+ * write ordered partials (k_parts * M * N * 4 bytes) that one pass sums in part
+ * order: bitwise reproducible.
  */
 qgemm_status qgemm_run(const qgemm_plan* plan, const void* A, const void* packed, void* C,
                        void* workspace, size_t workspace_bytes, void* stream);

@@ -20,11 +20,12 @@ class Case:
     """A seeded problem resident on the device, packed by the library."""
 
     def __init__(self, M, N, K, w_dtype, group_size=128, has_zeros=False, k_parts=1,
-                 deterministic=False, seed=1, problem=None):
+                 deterministic=False, seed=1, problem=None, split_auto=False):
         self.p = problem or synth.make_problem(M, N, K, w_dtype, group_size=group_size,
                                                has_zeros=has_zeros, seed=seed)
         p = self.p
-        self.q = QGemm(p.M, p.N, p.K, p.w_dtype, p.group_size, p.has_zeros, k_parts, deterministic)
+        self.q = QGemm(p.M, p.N, p.K, p.w_dtype, p.group_size, p.has_zeros, k_parts, deterministic,
+                       split_auto=split_auto)
         self.A = host_to_device(p.A)
         self.w = host_to_device(p.w)
         self.s = host_to_device(p.s)

@@ -54,7 +54,7 @@ def test_create_valid_formats():
     (dict(K=0), q.QGEMM_ERR_INVALID_ARG),
     (dict(k_parts=0), q.QGEMM_ERR_INVALID_ARG),
     (dict(k_parts=33), q.QGEMM_ERR_INVALID_ARG),          # 4096 / 128 = 32 units
-    (dict(flags=2), q.QGEMM_ERR_INVALID_ARG),
+    (dict(flags=4), q.QGEMM_ERR_INVALID_ARG),
     (dict(has_zeros=2), q.QGEMM_ERR_INVALID_ARG),
     (dict(group_size=-2), q.QGEMM_ERR_INVALID_ARG),
     (dict(a_dtype=99), q.QGEMM_ERR_INVALID_ARG),
@@ -96,16 +96,20 @@ def test_sizes_and_paths():
     plan, pb, wb = _create(M=9, N=100, k_parts=4)
     npad = 256
     assert pb == npad * 4096 // 2 + npad * 32 * 2
-    assert wb == 4 * 9 * 100 * 4                            # fp16 output: per-part partials
+    assert wb == 9 * 100 * 4                                # default split-K: one fp32 accumulator
     assert q.qgemm_plan_path(plan) == q.QGEMM_PATH_MFMA
     q.qgemm_destroy(plan)
     plan, pb, wb = _create(M=9, N=100, k_parts=4, flags=q.QGEMM_DETERMINISTIC)
     assert wb == 4 * 9 * 100 * 4                            # per-part partials
     q.qgemm_destroy(plan)
-    plan, pb, wb = _create(M=4100, N=8400, K=4096, k_parts=2)
-    assert wb == 4100 * 8400 * 4                            # partials past 256 MiB: fp32 atomics
+    plan, pb, wb = _create(M=9, N=100, k_parts=4, flags=q.QGEMM_SPLIT_AUTO)
+    assert wb == 4 * 9 * 100 * 4                            # auto: fp16 outputs take the partials
     q.qgemm_destroy(plan)
-    plan, pb, wb = _create(M=4100, N=8400, K=4096, k_parts=2, flags=q.QGEMM_DETERMINISTIC)
+    plan, pb, wb = _create(M=4100, N=8400, K=4096, k_parts=2, flags=q.QGEMM_SPLIT_AUTO)
+    assert wb == 4100 * 8400 * 4                            # ... until they pass 256 MiB
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(M=4100, N=8400, K=4096, k_parts=2,
+                           flags=q.QGEMM_DETERMINISTIC | q.QGEMM_SPLIT_AUTO)
     assert wb == 2 * 4100 * 8400 * 4                        # deterministic: partials regardless
     q.qgemm_destroy(plan)
     i8 = dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0)
@@ -113,7 +117,13 @@ def test_sizes_and_paths():
     assert wb == 0                                          # int32 atomics go straight into C
     q.qgemm_destroy(plan)
     plan, pb, wb = _create(M=128, k_parts=4, **i8)
-    assert wb == 4 * 128 * 4096 * 4                         # 128 rows and more: partials
+    assert wb == 0                                          # ... at any M by default
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(M=128, k_parts=4, flags=q.QGEMM_SPLIT_AUTO, **i8)
+    assert wb == 4 * 128 * 4096 * 4                         # auto: partials from 128 rows
+    q.qgemm_destroy(plan)
+    plan, pb, wb = _create(M=127, k_parts=4, flags=q.QGEMM_SPLIT_AUTO, **i8)
+    assert wb == 0                                          # ... atomics below
     q.qgemm_destroy(plan)
     plan, pb, wb = _create(w_dtype="u4", has_zeros=1, N=4096)
     assert pb == 4096 * 4096 // 2 + 32 * 4096 * 4           # (scale, zero) pairs
@@ -166,7 +176,7 @@ def test_null_and_misaligned_arguments_rejected_before_launch():
                         M=4, k_parts=2)
     i32, _, _ = _create(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0, M=4)
     try:
-        assert wb == 2 * 4 * 4096 * 4                          # fp16 output: per-part int32 partials
+        assert wb == 4 * 4096 * 4                              # fp16 output: one int32 accumulator
         for call in [lambda: q.qgemm_run(dq, 16, 16, 16, 16, wb, 0),
                      lambda: q.qgemm_run_ex(dq, 4, 16, 16, 0, 16, 16, wb, 0),
                      lambda: q.qgemm_run_scaled(dq, 4, 16, 16, 0, 16, 0, 16, 16, wb, 0),   # no row scales

@@ -19,37 +19,42 @@ def _bias(c, seed):
 
 
 BIAS_CASES = [
-    # M, N, K, w_dtype, g, zeros, k_parts, deterministic
-    (1, 300, 1024, "i4", 128, False, 1, False),    # GEMV, stored
-    (1, 72, 512, "u4", 128, True, 1, False),       # 16-column GEMV
-    (3, 136, 1024, "u4", 64, True, 3, False),      # GEMV, ordered partials + finalize
-    (5, 200, 1024, "i8", 0, False, 3, False),      # GEMV, int32 atomics onto the bias rows
-    (5, 200, 2048, "i2", 0, False, 2, True),       # GEMV, two-pass
-    (40, 264, 1024, "i4", 128, False, 1, False),   # direct-load MFMA, stored
-    (20, 264, 1024, "i8", 0, False, 3, False),     # matrix-core GEMV, int32 atomics onto the bias rows
-    (64, 72, 1024, "u4", 32, True, 1, False),      # LDS-staged MFMA (per-piece groups)
-    (130, 264, 768, "i4", 64, False, 3, True),     # LDS-staged MFMA, two-pass
-    (129, 136, 512, "i8", 0, False, 3, False),     # direct-load, int32 partials (128 rows and more)
-    (300, 520, 512, "f16", 0, False, 2, False),    # direct-load, ordered partials
-    (160, 264, 1024, "i2", 0, False, 1, False),    # direct-load int, stored
+    # M, N, K, w_dtype, g, zeros, k_parts, split-K reduction
+    (1, 300, 1024, "i4", 128, False, 1, "-"),         # GEMV, stored
+    (1, 72, 512, "u4", 128, True, 1, "-"),            # 16-column GEMV
+    (3, 136, 1024, "u4", 64, True, 3, "atomic"),      # GEMV, fp32 atomics + conversion pass
+    (3, 136, 1024, "u4", 64, True, 3, "det"),         # GEMV, ordered partials + summing pass
+    (5, 200, 1024, "i8", 0, False, 3, "atomic"),      # GEMV, int32 atomics onto the bias rows
+    (5, 200, 2048, "i2", 0, False, 2, "det"),         # GEMV, two-pass
+    (40, 264, 1024, "i4", 128, False, 1, "-"),        # direct-load MFMA, stored
+    (20, 264, 1024, "i8", 0, False, 3, "atomic"),     # matrix-core GEMV, int32 atomics onto the bias rows
+    (64, 72, 1024, "u4", 32, True, 1, "-"),           # LDS-staged MFMA (per-piece groups)
+    (130, 264, 768, "i4", 64, False, 3, "det"),       # LDS-staged MFMA, two-pass
+    (129, 136, 512, "i8", 0, False, 3, "auto"),       # direct-load, int32 partials (128 rows and more)
+    (129, 136, 512, "i8", 0, False, 3, "atomic"),     # direct-load, int32 atomics onto the bias rows
+    (300, 520, 512, "f16", 0, False, 2, "auto"),      # direct-load, ordered partials
+    (300, 520, 512, "f16", 0, False, 2, "atomic"),    # direct-load, fp32 atomics + conversion pass
+    (160, 264, 1024, "i2", 0, False, 1, "-"),         # direct-load int, stored
 ]
 
 
-@pytest.mark.parametrize("M,N,K,w_dtype,g,zeros,kp,det", BIAS_CASES)
-def test_bias_epilogue(M, N, K, w_dtype, g, zeros, kp, det):
-    say(f"case bias M={M} N={N} K={K} {w_dtype} g={g} kp={kp} det={det}")
-    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=5000 + M + N)
+@pytest.mark.parametrize("M,N,K,w_dtype,g,zeros,kp,split", BIAS_CASES)
+def test_bias_epilogue(M, N, K, w_dtype, g, zeros, kp, split):
+    say(f"case bias M={M} N={N} K={K} {w_dtype} g={g} kp={kp} split={split}")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=split == "det", split_auto=split == "auto",
+             seed=5000 + M + N)
     b = _bias(c, 5001 + N)
     assert_matches(c.run(bias=b), c.reference(bias=b), f"bias M={M} {w_dtype} kp={kp}")
 
 
-# split-K whose partials would pass 256 MiB keeps the atomic reductions: fp32 into the
-# zero-filled workspace (bias added by the finalize pass) and int32 onto the bias rows
+# the automatic choice keeps the atomic reductions where the partials would pass 256 MiB:
+# fp32 into the zero-filled workspace (bias added by the conversion pass) and int32 onto
+# the bias rows
 @pytest.mark.parametrize("w_dtype,g", [("i4", 128), ("i8", 0)])
 def test_bias_with_atomic_split(w_dtype, g):
     M, N, K = 4100, 8400, 256
     say(f"case bias atomic split M={M} N={N} K={K} {w_dtype} kp=2")
-    c = Case(M, N, K, w_dtype, g, False, k_parts=2, seed=5100)
+    c = Case(M, N, K, w_dtype, g, False, k_parts=2, seed=5100, split_auto=True)
     assert c.q.ws_bytes == (M * N * 4 if w_dtype == "i4" else 0)
     b = _bias(c, 5101)
     rng = np.random.default_rng(4)

@@ -160,15 +160,18 @@ int scale_mode(int fmt, int32_t group_size) {
   return SC_BLOCK;
 }
 
-// Split-K reduction without QGEMM_DETERMINISTIC: the fixed-order two-pass form
-// (partials [k_parts][M][N], then one pass that sums them in part order) whenever
-// its workspace stays modest and it is faster, else atomics into one accumulator.
-// fp16 outputs go through an fp32 accumulator either way, and zero-filling it plus
+// Split-K reduction.  By default the parts add into one accumulator with global
+// atomics (hidet issue #364, parallel-k with atomic reduction): fp32 atomics into
+// a zero-filled workspace followed by a conversion pass for fp16 outputs, int32
+// atomics straight into C.  QGEMM_DETERMINISTIC selects the fixed-order two-pass
+// form (partials [k_parts][M][N], then one pass that sums them in part order).
+// QGEMM_SPLIT_AUTO lets the library take whichever measured faster for the plan:
+// the two-pass form for fp16 outputs, where zero-filling the accumulator plus
 // contended fp32 atomics cost more than the partials (k_parts = 4: M = 1, LLaMA
 // shapes 10.5 -> 9.5 us; M = 128, N = 32000, K = 4096 105 -> 74 us; M = 512,
-// N = K = 16384 347 -> 291 us).  int32 outputs add atomically straight into C,
-// which wins below 128 rows (W2A8 M = 32: 34.2 against 37.9 us) and loses above
-// (W8A8 M = 512: 189 against 172 us).
+// N = K = 16384 347 -> 291 us), and for int32 outputs from 128 rows (W8A8
+// M = 512: 172 against 189 us; below that the atomics win, W2A8 M = 32: 34.2
+// against 37.9 us), while the partials stay within 256 MiB; atomics otherwise.
 #ifndef QG_TWO_PASS_MAX_BYTES
 #define QG_TWO_PASS_MAX_BYTES ((size_t)256 << 20)
 #endif
@@ -177,6 +180,7 @@ int scale_mode(int fmt, int32_t group_size) {
 #endif
 bool two_pass_split(int64_t M, size_t partial_bytes, bool out_f16, uint32_t flags) {
   if (flags & QGEMM_DETERMINISTIC) return true;
+  if (!(flags & QGEMM_SPLIT_AUTO)) return false;
   if (partial_bytes > QG_TWO_PASS_MAX_BYTES) return false;
   return out_f16 || M >= QG_TWO_PASS_INT_MIN_M;
 }
@@ -299,7 +303,7 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
     return QGEMM_ERR_INVALID_ARG;
   if (has_zeros != 0 && has_zeros != 1) return QGEMM_ERR_INVALID_ARG;
   if (k_parts < 1) return QGEMM_ERR_INVALID_ARG;
-  if (flags & ~QGEMM_DETERMINISTIC) return QGEMM_ERR_INVALID_ARG;
+  if (flags & ~(QGEMM_DETERMINISTIC | QGEMM_SPLIT_AUTO)) return QGEMM_ERR_INVALID_ARG;
   if (group_size < -1) return QGEMM_ERR_INVALID_ARG;
 
   // legal format tuples

@@ -19,7 +19,12 @@
 //   sum a*q = accE + accO/16 - (1024 + b)*SE - (64 + b)*SO,
 // where accE / accO are the dot products of the two nibble classes, SE / SO the
 // sums of the activations over the positions of each class, and b the
-// offset (8 for signed, 0 for unsigned).  int2 crumbs are masked in place
+// offset (8 for signed, 0 for unsigned).  Without scales the offsets are taken
+// off in fp16 instead (one exact packed subtraction per pair, so accE and accO sum
+// a*q and a*16q): unscaled sums over K = 16384 reach about 600, and the folded
+// accumulators, about a thousand times larger than the true sums, would round
+// beyond a 1e-2 error on the results near zero; a scale (0.005..0.02) shrinks that
+// error below it.  int2 crumbs are masked in place
 // (byte values c, 4c, 16c, and the two's complement top crumb as 64q), dotted
 // with int8 activations into four accumulators, and recombined exactly.  The
 // activation sums come from one load per lane and a DPP reduction per
@@ -76,7 +81,7 @@ __device__ __forceinline__ T lane_value(T v, int lane) {
   return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// VAR (int4 only): 0 folded, unscaled; 1 folded with one scale group per
+// VAR (int4 only): 0 unscaled (offsets taken off exactly); 1 folded with one scale group per
 // superblock; 2 as 1 with zero points; 3 exact per-element conversion with a
 // scale group per 32-position piece (group size 32 or 64).  int2 is always folded.
 template <int FMT, int MR, int VAR>
@@ -86,6 +91,9 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
   constexpr bool ZEROS = VAR == 2;
   constexpr bool FP = (FMT == FMT_I4 || FMT == FMT_U4 || FMT == FMT_F16);
   constexpr bool I4 = (FMT == FMT_I4 || FMT == FMT_U4);
+  // unscaled int4: offsets taken off per pair (exact), no activation class sums
+  constexpr bool EXACT = I4 && VAR == 0;
+  constexpr bool SUMS = FOLD && !EXACT;  // per-superblock activation class sums
   typedef typename std::conditional<FP, float, int>::type acc_t;
   // dwords of A per row: fp16 -> K/2, int8 -> K/4; every superblock is 64 dwords of A per row
   const int a_row_dw = FP ? a.K / 2 : a.K / 4;
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
       const uint32_t kbl = (uint32_t)row_of(min(j + u, cnt - 1));
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) s.w[u][kq] = stream_load(&Wl[kbl * sb_stride + kq * 16]);
-      if constexpr (FOLD) {
+      if constexpr (SUMS) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) s.as[u][m] = Av[m * a_row + kbl * A_DW_SB + sum_dw];
       }
@@ -171,6 +179,31 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
     }
   };
 
+  // offsets of the even (1024 + b) and odd (1024 + 16 b) nibble classes as fp16 pairs
+  const half2v OFS_E = as_h2(FMT == FMT_I4 ? 0x64086408u : 0x64006400u);
+  const half2v OFS_O = as_h2(FMT == FMT_I4 ? 0x64806480u : 0x64006400u);
+  auto exact = [&](half2v x, half2v o) { return EXACT ? x - o : x; };
+
+  // adds a superblock's nibble-class sums to the result: exact sums directly;
+  // folded ones less the offsets times the activation class sums, scaled
+  auto fold = [&](const float (&accE)[MR], const float (&accO)[MR], const uint32_t (&as)[MR], uint32_t sc) {
+    if constexpr (EXACT) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) tot[m] += accE[m] + accO[m] * 0.0625f;
+    } else {
+      constexpr float cE = (FMT == FMT_I4) ? 1032.f : 1024.f, cO = (FMT == FMT_I4) ? 72.f : 64.f;
+      const float s = h2f((uint16_t)(sc & 0xFFFFu)), z = h2f((uint16_t)(sc >> 16));
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const float h = half_wave_sums(__builtin_amdgcn_fdot2(as_h2(as[m]), as_h2(0x3C003C00u), 0.f, false));
+        const float SE = lane_value(h, 31), SO = lane_value(h, 63);
+        float v = accE[m] + accO[m] * 0.0625f - cE * SE - cO * SO;
+        if constexpr (ZEROS) v -= z * (SE + SO);
+        tot[m] += SCALED ? s * v : v;
+      }
+    }
+  };
+
   auto do_block = [&](const uint4 (&wv)[4], const uint32_t (&as)[MR], uint32_t sc, int kb) {
     if constexpr (I4 && FOLD) {
       const uint32_t MASK_E = 0x000F000Fu, MASK_O = 0x00F000F0u, EXP16 = 0x64006400u;
@@ -190,8 +223,10 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const uint32_t w = wd[t], w8 = w >> 8;
-          const half2v e0 = as_h2(and_or(w, MASK_E, EXP16)), o0 = as_h2(and_or(w, MASK_O, EXP16));
-          const half2v e1 = as_h2(and_or(w8, MASK_E, EXP16)), o1 = as_h2(and_or(w8, MASK_O, EXP16));
+          const half2v e0 = exact(as_h2(and_or(w, MASK_E, EXP16)), OFS_E);
+          const half2v o0 = exact(as_h2(and_or(w, MASK_O, EXP16)), OFS_O);
+          const half2v e1 = exact(as_h2(and_or(w8, MASK_E, EXP16)), OFS_E);
+          const half2v o1 = exact(as_h2(and_or(w8, MASK_O, EXP16)), OFS_O);
           const int base = kq * 16 + 4 * t;  // activation dword of positions 8t, 8t+1
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
@@ -202,16 +237,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
           }
         }
       }
-      constexpr float cE = (FMT == FMT_I4) ? 1032.f : 1024.f, cO = (FMT == FMT_I4) ? 72.f : 64.f;
-      const float s = h2f((uint16_t)(sc & 0xFFFFu)), z = h2f((uint16_t)(sc >> 16));
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        const float h = half_wave_sums(__builtin_amdgcn_fdot2(as_h2(as[m]), as_h2(0x3C003C00u), 0.f, false));
-        const float SE = lane_value(h, 31), SO = lane_value(h, 63);
-        float v = accE[m] + accO[m] * 0.0625f - cE * SE - cO * SO;
-        if constexpr (ZEROS) v -= z * (SE + SO);
-        tot[m] += SCALED ? s * v : v;
-      }
+      fold(accE, accO, as, sc);
     } else if constexpr (I4) {
       // exact per-element conversion, used when a superblock holds several groups
       constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;  // 1032 or 1024
@@ -356,10 +382,10 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const uint32_t w = wd[t], w8 = w >> 8;
-              e0[t] = as_h2(and_or(w, MASK_E, EXP16));
-              o0[t] = as_h2(and_or(w, MASK_O, EXP16));
-              e1[t] = as_h2(and_or(w8, MASK_E, EXP16));
-              o1[t] = as_h2(and_or(w8, MASK_O, EXP16));
+              e0[t] = exact(as_h2(and_or(w, MASK_E, EXP16)), OFS_E);
+              o0[t] = exact(as_h2(and_or(w, MASK_O, EXP16)), OFS_O);
+              e1[t] = exact(as_h2(and_or(w8, MASK_E, EXP16)), OFS_E);
+              o1[t] = exact(as_h2(and_or(w8, MASK_O, EXP16)), OFS_O);
             }
           },
           [&](int c, int m, const Chunk& ch) {
@@ -371,16 +397,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(RunArgs a) {
               accO[m] = __builtin_amdgcn_fdot2(o1[t], as_h2(ch.d[4 * t + 3]), accO[m], false);
             }
           });
-      constexpr float cE = (FMT == FMT_I4) ? 1032.f : 1024.f, cO = (FMT == FMT_I4) ? 72.f : 64.f;
-      const float s = h2f((uint16_t)(sc & 0xFFFFu)), z = h2f((uint16_t)(sc >> 16));
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        const float h = half_wave_sums(__builtin_amdgcn_fdot2(as_h2(as[m]), as_h2(0x3C003C00u), 0.f, false));
-        const float SE = lane_value(h, 31), SO = lane_value(h, 63);
-        float v = accE[m] + accO[m] * 0.0625f - cE * SE - cO * SO;
-        if constexpr (ZEROS) v -= z * (SE + SO);
-        tot[m] += SCALED ? s * v : v;
-      }
+      fold(accE, accO, as, sc);
     } else if constexpr (I4) {
       constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;  // 1032 or 1024
       const half2v hb = as_h2(bias);

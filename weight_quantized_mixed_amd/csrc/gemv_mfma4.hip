@@ -6,9 +6,10 @@
 // positions 0,2,4,6,1,3,5,7).  A superblock is loaded as stored (one 16-byte load,
 // piece l for lane l: step l / 16, column l % 16), and a 4 x 4 transpose of dwords
 // across the four 16-lane rows (two permlane32 and two permlane16 swaps) hands
-// lane (g, c) word g of the piece of every step; four v_and_or_b32 then turn slot
-// pairs (jj, jj + 4) into the fp16 pairs 1024 + q, with no subtraction (the bias
-// folding of the dot-product GEMV).  (Loading the words one dword per step instead,
+// lane (g, c) word g of the piece of every step; four v_and_or_b32 turn slot pairs
+// (jj, jj + 4) into the fp16 pairs 1024 + b + q (b the offset of the code: 8 for
+// signed int4, 0 for uint4) and one packed fp16 subtraction per pair takes
+// 1024 + b off, exactly.  (Loading the words one dword per step instead,
 // 16 loads of 256 bytes per wave for four superblocks, ran M = 8 in 40.9 against
 // 25.5 us.)  The A operand is a row of activations
 // (lane l: row l % 16 of the row block, positions 32 s + 8 g .. + 7), so one set
@@ -18,14 +19,16 @@
 // gives the CUs enough workgroups) and a k-part; its waves take the part's
 // superblock rows in turn and meet in LDS at the end.
 //
-// Per superblock and column block the MFMAs accumulate T = sum a (1024 + b + q),
-// with b the offset of the code (8 for signed int4, 0 for uint4), into a
-// temporary; three more MFMAs per superblock against a B of fp16 ones give the
-// row sums S = sum a, and the superblock is folded into the result as
-//   acc += s * (T - (1024 + b + z) * S)                    (all in fp32)
-// which is sum a (q - z) s for its scale group (z = 0 without zero points, s = 1
-// without scales).  Products a (1024 + q) are exact in fp32 and a superblock sums
-// only 128 of them, so the fold loses no more than fp32 rounding of T.
+// Without scales the MFMAs accumulate sum a q straight into the result.  With
+// scales they accumulate T = sum a q per superblock and column block into a
+// temporary, folded as acc += s * T; with zero points three more MFMAs per
+// superblock against a B of fp16 ones give the row sums S = sum a, and the fold is
+//   acc += s * (T - z * S)                                  (all in fp32)
+// which is sum a (q - z) s for its scale group.  Products a q are exact in fp32
+// and the partial sums stay as small as the result's own terms: keeping the
+// 1024 + b offsets in the operands (and removing them once per superblock) would
+// make T about a thousand times larger than the true sum, and its fp32 rounding
+// alone exceeds a 1e-2 error at K = 16384 without scales.
 // Groups of whole superblocks (or one group over K) only; 32- and 64-position
 // groups take the dot-product GEMV.
 #include "qgemm_internal.hpp"
@@ -33,6 +36,7 @@
 namespace qg {
 namespace {
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
@@ -77,7 +81,6 @@ template <int FMT, int MB, int VAR, int CB>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs a) {
   constexpr int KB = 128, NS = 4;  // positions and 32-position MFMA steps per superblock
   constexpr bool SCALED = VAR >= 1, ZEROS = VAR == 2;
-  constexpr float BIAS = FMT == FMT_I4 ? 1032.f : 1024.f;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -130,6 +133,11 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
     for (int cb = 0; cb < CB; ++cb) acc[r][cb] = float4v{0.f, 0.f, 0.f, 0.f};
 
   const uint4 ONES = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  // 1024 + b in both halves: (1024 + b + q) - (1024 + b) = q exactly in fp16
+  const half2v OFS = __builtin_bit_cast(half2v, FMT == FMT_I4 ? 0x64086408u : 0x64006400u);
+  auto code = [&](uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, and_or(x, 0x000F000Fu, 0x64006400u)) - OFS);
+  };
   auto consume = [&](const Stage& s) {
     // packed word of each column block and step: word g of the piece of step t
     uint32_t w[CB][NS];
@@ -140,6 +148,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
 #pragma unroll
       for (int t = 0; t < NS; ++t) w[cb][t] = x[t];
     }
+    // scaled: per-superblock sums T (and row sums S with zero points); unscaled:
+    // straight into acc
     float4v T[MB][CB], S[MB];
 #pragma unroll
     for (int r = 0; r < MB; ++r) {
@@ -152,23 +162,31 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_mfma4_kernel(RunArgs
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const uint32_t wd = w[cb][t];
-        const uint4 B = make_uint4(and_or(wd, 0x000F000Fu, 0x64006400u), and_or(wd >> 4, 0x000F000Fu, 0x64006400u),
-                                   and_or(wd >> 8, 0x000F000Fu, 0x64006400u), and_or(wd >> 12, 0x000F000Fu, 0x64006400u));
+        const uint4 B = make_uint4(code(wd), code(wd >> 4), code(wd >> 8), code(wd >> 12));
 #pragma unroll
-        for (int r = 0; r < MB; ++r) T[r][cb] = mfma(s.av[r][t], B, T[r][cb]);
+        for (int r = 0; r < MB; ++r) {
+          if constexpr (SCALED) T[r][cb] = mfma(s.av[r][t], B, T[r][cb]);
+          else acc[r][cb] = mfma(s.av[r][t], B, acc[r][cb]);
+        }
       }
+      if constexpr (ZEROS) {
 #pragma unroll
-      for (int r = 0; r < MB; ++r) S[r] = mfma(s.av[r][t], ONES, S[r]);
+        for (int r = 0; r < MB; ++r) S[r] = mfma(s.av[r][t], ONES, S[r]);
+      }
     }
+    if constexpr (SCALED) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      float sc = 1.f, c = BIAS;
-      if constexpr (SCALED) sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(s.sc[cb] & 0xFFFFu));
-      if constexpr (ZEROS) c += (float)__builtin_bit_cast(_Float16, (uint16_t)(s.sc[cb] >> 16));
+      for (int cb = 0; cb < CB; ++cb) {
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(s.sc[cb] & 0xFFFFu));
+        const float z = ZEROS ? (float)__builtin_bit_cast(_Float16, (uint16_t)(s.sc[cb] >> 16)) : 0.f;
 #pragma unroll
-      for (int r = 0; r < MB; ++r)
+        for (int r = 0; r < MB; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[r][cb][i] += sc * (T[r][cb][i] - c * S[r][i]);
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (ZEROS) acc[r][cb][i] += sc * (T[r][cb][i] - z * S[r][i]);
+            else acc[r][cb][i] += sc * T[r][cb][i];
+          }
+      }
     }
   };
 

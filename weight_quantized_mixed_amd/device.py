@@ -55,10 +55,12 @@ class QGemm:
 
     dequant_output: int8 activations with an fp16 output dequantised by per-row
     and per-column scales (run_scaled) instead of the int32 accumulator.
+    Split-K (k_parts > 1) reduces with atomics, or with ordered partials when
+    deterministic; split_auto lets the library pick the faster of the two.
     """
 
     def __init__(self, M, N, K, w_dtype, group_size=0, has_zeros=False, k_parts=1,
-                 deterministic=False, device="cuda", dequant_output=False):
+                 deterministic=False, device="cuda", dequant_output=False, split_auto=False):
         self.M, self.N, self.K, self.w_dtype = int(M), int(N), int(K), w_dtype
         self.a_dtype = A_DTYPE[w_dtype]
         self.out_dtype, self.accum_dtype = OUT_DTYPE[self.a_dtype]
@@ -67,7 +69,7 @@ class QGemm:
                 raise ValueError("dequant_output is for int8 activations")
             self.out_dtype = "f16"
         self.device = torch.device(device)
-        flags = _q.QGEMM_DETERMINISTIC if deterministic else 0
+        flags = (_q.QGEMM_DETERMINISTIC if deterministic else 0) | (_q.QGEMM_SPLIT_AUTO if split_auto else 0)
         self.plan, self.packed_bytes, self.ws_bytes = _q.qgemm_create(
             M, N, K, self.a_dtype, w_dtype, self.out_dtype, self.accum_dtype, group_size,
             int(bool(has_zeros)), k_parts, flags)

@@ -19,6 +19,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported format or shape",
           3: "out of host memory", 4: "device launch failed"}
 QGEMM_OK, QGEMM_ERR_INVALID_ARG, QGEMM_ERR_UNSUPPORTED, QGEMM_ERR_NO_MEMORY, QGEMM_ERR_DEVICE = range(5)
 QGEMM_DETERMINISTIC = 1
+QGEMM_SPLIT_AUTO = 2
 QGEMM_PATH_GEMV, QGEMM_PATH_MFMA = 1, 2
 
 EXPORTED = ("qgemm_create", "qgemm_pack_weights", "qgemm_run", "qgemm_run_ex", "qgemm_run_scaled",
