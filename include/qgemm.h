@@ -184,6 +184,27 @@ qgemm_status qgemm_run_ex(const qgemm_plan* plan, int64_t M, const void* A, cons
                           void* stream);
 
 /*
+ * qgemm_run_ex without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Split-K runs in a fixed scratch array inside the
+ * library, one per GPU, of QGEMM_NOALLOC_MAX_SCRATCH bytes, which each GPU the
+ * library runs on holds until the process ends; this call itself allocates
+ * nothing.  It needs run-time M * N * 4 bytes of scratch for atomic split-K with
+ * fp16 output, k_parts * M * N * 4 for the two-pass reduction, none otherwise;
+ * more than the maximum returns QGEMM_ERR_UNSUPPORTED before any device call.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in
+ * time on one GPU (other streams, other threads) race and must be serialised by
+ * the caller.  The stream must belong to the current device.  Plans with
+ * dequantised int8 output (qgemm_run_scaled) are rejected (QGEMM_ERR_INVALID_ARG).
+ *   M, A, packed, bias, C, stream: as in qgemm_run_ex.
+ * The first call that needs scratch on a device looks up its address
+ * (QGEMM_ERR_DEVICE if that fails).
+ */
+#define QGEMM_NOALLOC_MAX_SCRATCH ((size_t)32 << 20)
+qgemm_status qgemm_run_noalloc(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,
+                               const void* bias, void* C, void* stream);
+
+/*
  * int8 activations with fp16 output (plans created with the tuple
  * (I8, I8 | I2, F16, I32)): C[m, n] = fp16(acc[m, n] * row_scales[m] *
  * col_scales[n] (+ bias[n])), the dequantising epilogue of the int8

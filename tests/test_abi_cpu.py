@@ -249,3 +249,29 @@ def test_pages_grid_maps_to_plans():
         want = q.QGEMM_PATH_GEMV if args["M"] <= 8 else q.QGEMM_PATH_MFMA
         assert q.qgemm_plan_path(plan) == want
         q.qgemm_destroy(plan)
+
+
+def test_noalloc_rejects_before_any_device_call():
+    """qgemm_run_noalloc checks its arguments and the scratch it would need before it
+    looks up the scratch array or launches anything."""
+    assert q.NOALLOC_MAX_SCRATCH == 32 << 20
+    big, _, wb = _create(M=4096, N=16384, K=4096, k_parts=2)   # fp32 atomics: 256 MiB of scratch
+    dq, _, _ = _create(a_dtype="i8", w_dtype="i8", out_dtype="f16", accum_dtype="i32", group_size=0, M=4)
+    try:
+        assert wb == 4096 * 16384 * 4
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_run_noalloc(big, 4096, 16, 16, 0, 16, 0)
+        assert e.value.status == q.QGEMM_ERR_UNSUPPORTED
+        for M in (0, 4097):
+            with pytest.raises(q.QGemmError) as e:
+                q.qgemm_run_noalloc(big, M, 16, 16, 0, 16, 0)
+            assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_run_noalloc(dq, 4, 16, 16, 0, 16, 0)          # needs its scales
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+        with pytest.raises(q.QGemmError) as e:
+            q.qgemm_run_noalloc(0, 1, 16, 16, 0, 16, 0)
+        assert e.value.status == q.QGEMM_ERR_INVALID_ARG
+    finally:
+        q.qgemm_destroy(big)
+        q.qgemm_destroy(dq)

@@ -4,6 +4,7 @@
 // The arguments follow the problem statement of BitBLAS issue #252
 // (reproduction script: M, N, K, A_dtype, W_dtype, out_dtype, accum_dtype,
 // group_size, with_scaling, with_zeros) plus hidet issue #364's k-parts.
+#include <mutex>
 #include <new>
 
 #include "qgemm_internal.hpp"
@@ -247,13 +248,22 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
 
 namespace {
 
+// workspace bytes a run of M rows uses (the plan's workspace_bytes is this at its M)
+size_t run_ws_bytes(const qgemm_plan* p, int64_t M) {
+  if (p->k_parts == 1) return 0;
+  const size_t mn4 = (size_t)M * (size_t)p->N * 4;
+  if (p->two_pass) return mn4 * (size_t)p->k_parts;
+  return p->out_dtype == QGEMM_F16 ? mn4 : 0;
+}
+
 // one run: the split-K fill, the kernel chosen for M rows, the finalize pass
 qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const void* packed, const void* bias,
                       const float* row_scales, const float* col_scales, void* C, void* workspace,
                       size_t workspace_bytes, void* stream) {
   if (!plan || !A || !packed || !C) return QGEMM_ERR_INVALID_ARG;
   if (M < 1 || M > plan->M) return QGEMM_ERR_INVALID_ARG;
-  if (plan->ws_bytes && (!workspace || workspace_bytes < plan->ws_bytes)) return QGEMM_ERR_INVALID_ARG;
+  const size_t need = run_ws_bytes(plan, M);
+  if (need && (!workspace || workspace_bytes < need)) return QGEMM_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(packed) |
        reinterpret_cast<uintptr_t>(workspace)) & 15)
     return QGEMM_ERR_INVALID_ARG;
@@ -286,6 +296,38 @@ qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const vo
 }
 
 bool dequant_plan(const qgemm_plan* p) { return p->a_dtype == QGEMM_I8 && p->out_dtype == QGEMM_F16; }
+
+}  // namespace
+
+// Scratch of qgemm_run_noalloc: a fixed array in device memory, one copy per GPU
+// (each holds it until the process ends).  In host code `scratch` names only a
+// stand-in for the symbol; the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[QGEMM_NOALLOC_MAX_SCRATCH];
+
+namespace {
+
+constexpr int QG_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[QG_MAX_DEVICES] = {};
+
+// device address of the current device's scratch array (looked up on first use)
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= QG_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -375,6 +417,20 @@ qgemm_status qgemm_run_ex(const qgemm_plan* plan, int64_t M, const void* A, cons
                           const void* bias, void* C, void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan || dequant_plan(plan)) return QGEMM_ERR_INVALID_ARG;  // those need their scales
   return run_impl(plan, M, A, packed, bias, nullptr, nullptr, C, workspace, workspace_bytes, stream);
+}
+
+qgemm_status qgemm_run_noalloc(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,
+                               const void* bias, void* C, void* stream) {
+  if (!plan || dequant_plan(plan)) return QGEMM_ERR_INVALID_ARG;
+  if (M < 1 || M > plan->M) return QGEMM_ERR_INVALID_ARG;
+  const size_t need = run_ws_bytes(plan, M);
+  if (need > QGEMM_NOALLOC_MAX_SCRATCH) return QGEMM_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (need) {
+    (void)hipGetLastError();
+    if (scratch_of_current_device(&ws) != hipSuccess) return QGEMM_ERR_DEVICE;
+  }
+  return run_impl(plan, M, A, packed, bias, nullptr, nullptr, C, ws, need, stream);
 }
 
 qgemm_status qgemm_run_scaled(const qgemm_plan* plan, int64_t M, const void* A, const void* packed,

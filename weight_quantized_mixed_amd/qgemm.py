@@ -22,8 +22,10 @@ QGEMM_DETERMINISTIC = 1
 QGEMM_SPLIT_AUTO = 2
 QGEMM_PATH_GEMV, QGEMM_PATH_MFMA = 1, 2
 
-EXPORTED = ("qgemm_create", "qgemm_pack_weights", "qgemm_run", "qgemm_run_ex", "qgemm_run_scaled",
-            "qgemm_quantize_rows", "qgemm_destroy", "qgemm_plan_path", "qgemm_status_string")
+EXPORTED = ("qgemm_create", "qgemm_pack_weights", "qgemm_run", "qgemm_run_ex", "qgemm_run_noalloc",
+            "qgemm_run_scaled", "qgemm_quantize_rows", "qgemm_destroy", "qgemm_plan_path",
+            "qgemm_status_string")
+NOALLOC_MAX_SCRATCH = 32 << 20
 
 
 class QGemmError(RuntimeError):
@@ -63,6 +65,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qgemm_run.restype = c_i32
     lib.qgemm_run_ex.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
     lib.qgemm_run_ex.restype = c_i32
+    lib.qgemm_run_noalloc.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p]
+    lib.qgemm_run_noalloc.restype = c_i32
     lib.qgemm_run_scaled.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
     lib.qgemm_run_scaled.restype = c_i32
     lib.qgemm_quantize_rows.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_p]
@@ -114,6 +118,13 @@ def qgemm_run_ex(plan, M, A, packed, bias, C, workspace, workspace_bytes, stream
                              workspace or None, int(workspace_bytes), stream or None)
     if st != QGEMM_OK:
         raise QGemmError(st, "qgemm_run_ex")
+
+
+def qgemm_run_noalloc(plan, M, A, packed, bias, C, stream=0):
+    st = load().qgemm_run_noalloc(plan, int(M), A or None, packed or None, bias or None, C or None,
+                                  stream or None)
+    if st != QGEMM_OK:
+        raise QGemmError(st, "qgemm_run_noalloc")
 
 
 def qgemm_run_scaled(plan, M, A, packed, row_scales, col_scales, bias, C, workspace, workspace_bytes,
