@@ -100,9 +100,14 @@ typedef enum {
  * configuration (M, N, K, A_dtype, W_dtype, out_dtype, accum_dtype, group_size,
  * with_scaling as group_size != 0, with_zeros) plus hidet issue #364's k-parts.
  * No device call.
- *   M, N, K       problem sizes, each >= 1.  K must be a multiple of the block
- *                 depth of the weight format: 128 (I4/U4), 256 (I2), 64 (I8),
- *                 32 (F16), else QGEMM_ERR_UNSUPPORTED.
+ *   M, N, K       problem sizes, each >= 1.  K must be a multiple of the values
+ *                 per canonical word: 8 (I4/U4), 16 (I2), 1 (I8/F16), and of
+ *                 group_size when that is > 0, else QGEMM_ERR_UNSUPPORTED.  The
+ *                 kernels work on whole blocks of 128 (I4/U4), 256 (I2), 64 (I8)
+ *                 or 32 (F16) positions: when K is not a multiple of that depth,
+ *                 the blob is zero-padded and every run first copies A into the
+ *                 workspace with its rows zero-padded (the workspace then also
+ *                 holds M * roundup(K, depth) activation elements).
  *   group_size    0 = no scaling (with_scaling False), -1 = one group per output
  *                 column over all of K, g > 0 = groups of g along K.  Scaled
  *                 formats are I4/U4 only; g > 0 must divide K and be a multiple
@@ -113,7 +118,7 @@ typedef enum {
  *                 (default) or by ordered partials and one summing pass
  *                 (QGEMM_DETERMINISTIC; see qgemm_run).  At most K / unit, where
  *                 unit = group_size when it is a multiple of the block depth
- *                 (and larger), else the block depth.
+ *                 (and larger), else the block depth (K rounded up to it).
  *   flags         0, or QGEMM_DETERMINISTIC and / or QGEMM_SPLIT_AUTO.
  *   packed_bytes  out: size of the packed blob for qgemm_pack_weights/qgemm_run.
  *   workspace_bytes out: size of the device workspace qgemm_run needs (0 if none).
@@ -141,12 +146,13 @@ qgemm_status qgemm_pack_weights(const qgemm_plan* plan, const void* w, const voi
  * C = A . dequant(W) on `stream` (the quantized matmul of hidet issue #364 and
  * BitBLAS issue #252; int8 x int8 / int2 products accumulate and return int32,
  * Triton PR #3595).
- *   A          device, [M, K] fp16 or int8, 16-byte aligned.
+ *   A          device, [M, K] fp16 or int8, 16-byte aligned (rows are K elements
+ *              apart, whatever their alignment).
  *   packed     device, the blob written by qgemm_pack_weights.
  *   C          device, [M, N] fp16 or int32; fully overwritten.
  *   workspace  device, >= workspace_bytes (may be NULL when that is 0),
- *              16-byte aligned; scratch for split-K, its contents on entry are
- *              ignored.
+ *              16-byte aligned; scratch for split-K and padded activations, its
+ *              contents on entry are ignored.
  * Split-K (k_parts > 1) reduces the parts with global atomics unless a flag says
  * otherwise: fp16 outputs add fp32 partials into the zero-filled workspace
  * (M * N * 4 bytes), which one more pass rounds into C; int32 outputs add

@@ -66,9 +66,11 @@ def test_create_valid_formats():
     (dict(w_dtype="u4", has_zeros=1, group_size=0), q.QGEMM_ERR_UNSUPPORTED),
     (dict(group_size=48), q.QGEMM_ERR_UNSUPPORTED),         # not a multiple of 32
     (dict(group_size=96, K=4096), q.QGEMM_ERR_UNSUPPORTED),  # does not divide K
-    (dict(K=4000), q.QGEMM_ERR_UNSUPPORTED),                # not a multiple of 128
-    (dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=0, K=4224),
-     q.QGEMM_ERR_UNSUPPORTED),                              # int2 blocks are 256 deep
+    (dict(K=4000), q.QGEMM_ERR_UNSUPPORTED),                # g = 128 does not divide K
+    (dict(K=4100, group_size=0), q.QGEMM_ERR_UNSUPPORTED),  # not whole int4 words (8 values)
+    (dict(K=4100, group_size=-1), q.QGEMM_ERR_UNSUPPORTED),
+    (dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=0, K=4104),
+     q.QGEMM_ERR_UNSUPPORTED),                              # not whole int2 words (16 values)
     (dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=128),
      q.QGEMM_ERR_UNSUPPORTED),                              # int formats are unscaled
 ])
@@ -275,3 +277,39 @@ def test_noalloc_rejects_before_any_device_call():
     finally:
         q.qgemm_destroy(big)
         q.qgemm_destroy(dq)
+
+
+@pytest.mark.parametrize("kw,Kpad", [
+    (dict(K=4104, group_size=0), 4224),                      # int4: whole words, not whole 128-blocks
+    (dict(K=4104, group_size=-1, w_dtype="u4", has_zeros=1), 4224),
+    (dict(K=4128, group_size=96), 4224),                     # groups of 96: 44 scale rows stored
+    (dict(K=8, group_size=0), 128),
+    (dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=0, K=4112), 4352),
+    (dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0, K=4100), 4160),
+    (dict(w_dtype="f16", group_size=0, K=4099), 4128),
+])
+def test_k_granularity_pads_to_whole_blocks(kw, Kpad):
+    """K needs only whole canonical words and whole groups: the blob is padded to whole
+    blocks and the workspace gains the zero-padded activation rows."""
+    M, N = 3, 100
+    plan, pb, wb = _create(M=M, N=N, **kw)
+    try:
+        w = kw.get("w_dtype", "i4")
+        bits = {"i4": 4, "u4": 4, "i2": 2, "i8": 8, "f16": 16}[w]
+        g = kw["group_size"]
+        rows = 0 if g == 0 else 1 if g < 0 else -(-Kpad // g)
+        per = 4 if kw.get("has_zeros") else 2
+        assert pb == 256 * Kpad * bits // 8 + rows * 256 * per
+        esz = 1 if kw.get("a_dtype") == "i8" else 2
+        assert wb == M * Kpad * esz
+    finally:
+        q.qgemm_destroy(plan)
+    # with split-K the padded rows follow the accumulator, 256-byte aligned
+    if Kpad == 128:
+        return                                                 # one block: no split
+    plan, pb, wb = _create(M=M, N=N, k_parts=2, **kw)
+    try:
+        acc = M * N * 4 if kw.get("a_dtype") != "i8" else 0
+        assert wb == -(-acc // 256) * 256 + M * Kpad * (1 if kw.get("a_dtype") == "i8" else 2)
+    finally:
+        q.qgemm_destroy(plan)

@@ -303,3 +303,53 @@ def test_graph_replays_match_eager(M, N, K, w_dtype, g, zeros, kp, det):
             assert np.array_equal(got, eager), f"replay {r} differs from the eager result"
         c.run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- K not a multiple of the block depth
+# K needs only whole canonical words (8 int4, 16 int2 values) and whole groups: the
+# blob pads K to whole blocks with zero codes (zero scales for 96-position groups past
+# K) and each run reads activations zero-padded in the workspace.
+ODD_K = [
+    # M, N, K, w_dtype, g, zeros
+    (1, 300, 4104, "i4", 0, False),       # dot-product GEMV
+    (1, 300, 4104, "i4", -1, False),
+    (3, 300, 4104, "u4", -1, True),       # matrix-core int4 GEMV
+    (8, 136, 4104, "i4", 0, False),
+    (20, 264, 4104, "i4", -1, False),
+    (40, 264, 4104, "u4", -1, True),      # direct-load MFMA
+    (300, 520, 4104, "i4", 0, False),
+    (1, 200, 4128, "i4", 96, False),      # per-piece groups, one padded scale row
+    (40, 136, 4128, "u4", 96, True),      # LDS-staged MFMA
+    (1, 200, 4112, "i2", 0, False),
+    (5, 72, 4112, "i2", 0, False),
+    (40, 264, 4112, "i2", 0, False),
+    (1, 300, 4100, "i8", 0, False),       # int8 rows 4100 bytes apart (not 16-byte aligned)
+    (8, 136, 4100, "i8", 0, False),
+    (130, 264, 4100, "i8", 0, False),
+    (1, 200, 4099, "f16", 0, False),      # fp16 rows 8198 bytes apart
+    (33, 200, 4099, "f16", 0, False),
+    (7, 72, 1000, "f16", 0, False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,w_dtype,g,zeros", ODD_K)
+@pytest.mark.parametrize("kp,det", [(1, False), (3, False), (3, True)])
+def test_k_not_a_multiple_of_the_block(M, N, K, w_dtype, g, zeros, kp, det):
+    say(f"odd K M={M} N={N} K={K} {w_dtype} g={g} zeros={zeros} kp={kp} det={det}")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, deterministic=det, seed=M * 7 + N + K)
+    assert_matches(c.run(), c.reference(), f"odd K M={M} N={N} K={K} {w_dtype} kp={kp}")
+
+
+def test_k_of_one_int4_word():
+    c = Case(3, 100, 8, "i4", 0, False, seed=31)
+    assert_matches(c.run(), c.reference(), "K = 8")
+
+
+@pytest.mark.parametrize("w_dtype,g,zeros,kp", [("i4", 0, False, 1), ("u4", -1, True, 3), ("i8", 0, False, 2)])
+def test_k_tail_with_fewer_rows_and_bias(w_dtype, g, zeros, kp):
+    """qgemm_run_ex on fewer rows than the plan's, with a bias, at a padded K."""
+    K = {"i4": 4104, "u4": 4104, "i8": 4100}[w_dtype]
+    c = Case(40, 264, K, w_dtype, g, zeros, k_parts=kp, seed=32 + kp)
+    b = synth.draw_bias(264, c.q.out_dtype, 33)
+    for M in (1, 7, 40):
+        assert_matches(c.run(M=M, bias=b), c.reference(rows=np.arange(M), bias=b), f"rows {M} K={K}")

@@ -30,6 +30,8 @@ CASES = [
     (32, 2048, 4096, "i8", 0, False, 4, "atomic"),     # int32 atomics straight into C (no scratch)
     (300, 1000, 1024, "i2", 0, False, 4, "auto"),      # int32 ordered partials in scratch
     (4, 1000, 1024, "i4", 0, False, 1, "-"),           # no split: no scratch at all
+    (8, 1000, 4104, "i4", 0, False, 3, "atomic"),      # K padded: activation rows in scratch too
+    (40, 264, 4100, "i8", 0, False, 1, "-"),           # K padded, no split
 ]
 
 

@@ -56,15 +56,18 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
   L->fmt = fmt;
   L->N = N;
   L->K = K;
+  L->Kpad = round_up(K, kb_of(fmt));
   L->Npad = round_up(N, 256);
   L->NB = L->Npad / 16;
-  L->nkb = K / kb_of(fmt);
+  L->nkb = L->Kpad / kb_of(fmt);
   L->group_size = g;
   L->G = g == 0 ? 0 : g < 0 ? 1 : K / g;
+  // groups smaller than a superblock are indexed per 32-position piece up to Kpad
+  L->G_store = g > 0 ? (L->Kpad + g - 1) / g : L->G;
   L->zeros = zeros;
   L->w_bytes = (size_t)L->nkb * (size_t)L->NB * 1024;
   L->s_offset = (size_t)round_up((int64_t)L->w_bytes, 256);
-  L->s_bytes = (size_t)L->G * (size_t)L->Npad * (zeros ? 4 : 2);
+  L->s_bytes = (size_t)L->G_store * (size_t)L->Npad * (zeros ? 4 : 2);
   L->total = L->s_offset + L->s_bytes;
   return QGEMM_OK;
 }
@@ -248,12 +251,20 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
 
 namespace {
 
-// workspace bytes a run of M rows uses (the plan's workspace_bytes is this at its M)
-size_t run_ws_bytes(const qgemm_plan* p, int64_t M) {
+// workspace of a run of M rows (the plan's workspace_bytes is this at its M): the
+// split-K accumulator or partials, then (K not a multiple of the superblock depth)
+// the activations zero-padded to Kpad, 256-byte aligned
+size_t split_ws_bytes(const qgemm_plan* p, int64_t M) {
   if (p->k_parts == 1) return 0;
   const size_t mn4 = (size_t)M * (size_t)p->N * 4;
   if (p->two_pass) return mn4 * (size_t)p->k_parts;
   return p->out_dtype == QGEMM_F16 ? mn4 : 0;
+}
+size_t a_esz(const qgemm_plan* p) { return p->a_dtype == QGEMM_F16 ? 2 : 1; }
+size_t pad_offset(const qgemm_plan* p, int64_t M) { return (size_t)round_up((int64_t)split_ws_bytes(p, M), 256); }
+size_t run_ws_bytes(const qgemm_plan* p, int64_t M) {
+  if (p->L.Kpad == p->K) return split_ws_bytes(p, M);
+  return pad_offset(p, M) + (size_t)M * (size_t)p->L.Kpad * a_esz(p);
 }
 
 // one run: the split-K fill, the kernel chosen for M rows, the finalize pass
@@ -279,7 +290,15 @@ qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const vo
   a.col_scale = col_scales;
   (void)hipGetLastError();  // clear an error left by an unrelated earlier call on this thread
   hipError_t e = hipSuccess;
-  if (a.out_mode == OUT_ATOMIC)
+  if (plan->L.Kpad != plan->K) {
+    // K is not a multiple of the superblock depth: the kernels read the activations
+    // zero-padded to Kpad (the blob holds zero codes there)
+    void* Ap = static_cast<char*>(workspace) + pad_offset(plan, M);
+    e = launch_pad_rows(A, Ap, M, plan->K, plan->L.Kpad, (int)a_esz(plan), st);
+    a.A = Ap;
+    a.K = (int32_t)plan->L.Kpad;
+  }
+  if (e == hipSuccess && a.out_mode == OUT_ATOMIC)
     e = out_f16 ? launch_fill_zero(workspace, (size_t)M * plan->N * 4, st)  // fp32 / int32 accumulator
         : bias  ? launch_fill_bias(a, st)
                 : launch_fill_zero(C, (size_t)M * plan->N * 4, st);
@@ -364,14 +383,19 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   if (!scaled_fmt && group_size != 0) return QGEMM_ERR_UNSUPPORTED;
   if (has_zeros && (fmt != FMT_U4 || group_size == 0)) return QGEMM_ERR_UNSUPPORTED;
   if (group_size > 0 && (K % group_size != 0 || group_size % 32 != 0)) return QGEMM_ERR_UNSUPPORTED;
-  if (K % KB != 0) return QGEMM_ERR_UNSUPPORTED;
+  // K: whole canonical words (8 int4, 16 int2 values); the kernels run on K padded
+  // to whole superblocks
+  if (K % pack_factor(fmt) != 0) return QGEMM_ERR_UNSUPPORTED;
+  const int64_t Kpad = round_up(K, KB);
+  if (Kpad > INT32_MAX) return QGEMM_ERR_UNSUPPORTED;
 
   // kernels index the blob with 32-bit uint4 offsets
-  if ((N + 255) / 256 * 256 / 16 * (K / KB) * 64 >= INT32_MAX) return QGEMM_ERR_UNSUPPORTED;
+  if ((N + 255) / 256 * 256 / 16 * (Kpad / KB) * 64 >= INT32_MAX) return QGEMM_ERR_UNSUPPORTED;
 
   // split unit: whole superblocks, and whole groups when groups are whole superblocks
+  // (then K is a multiple of the group, so Kpad = K)
   const int64_t unit = scale_mode(fmt, group_size) == SC_BLOCK && group_size > KB ? group_size : KB;
-  const int64_t n_units = K / unit;
+  const int64_t n_units = Kpad / unit;
   if (k_parts > n_units) return QGEMM_ERR_INVALID_ARG;
 
   qgemm_plan* p = new (std::nothrow) qgemm_plan();
@@ -393,9 +417,7 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   p->ch = choose(p, M);
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   p->two_pass = k_parts > 1 && two_pass_split(M, mn4 * (size_t)k_parts, out_dtype == QGEMM_F16, flags);
-  if (k_parts == 1) p->ws_bytes = 0;
-  else if (p->two_pass) p->ws_bytes = mn4 * (size_t)k_parts;
-  else p->ws_bytes = out_dtype == QGEMM_F16 ? mn4 : 0;  // int32 output: atomics straight into C
+  p->ws_bytes = run_ws_bytes(p, M);  // int32 output with atomics: none (straight into C)
   if (packed_bytes) *packed_bytes = p->L.total;
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
   *out = p;

@@ -1,5 +1,6 @@
-// One-time repacking of canonical "nt" weights into the gfx950 superblock blob,
-// and of the [N, G] scale / zero tables into [G][Npad] rows.  The storage
+// One-time repacking of canonical "nt" weights into the gfx950 superblock blob
+// (K padded with zero codes to whole superblocks), and of the [N, G] scale / zero
+// tables into [G_store][Npad] rows.  The storage
 // format is the problem statement's transposed weight (BitBLAS issue #252,
 // reproduction script, layout "nt"); the pre-shuffled, backend-specific packed
 // tensor follows the "dtype + packing_format" structure of torchao issue #2752.
@@ -10,6 +11,42 @@ namespace {
 
 // slot (0..7) of a word that receives position p (0..7): evens first, then odds
 __device__ __forceinline__ int i4_slot(int p) { return (p & 1) ? 4 + (p >> 1) : (p >> 1); }
+
+// The 16 canonical bytes of column n from reduction position k0 on (one piece):
+// four words of 8 int4 / 16 int2 values, 16 int8 values or 8 fp16 values.
+// Positions at or past K read as zero codes; rows that are not 16-byte aligned
+// (K not a multiple of 32 int4 / 64 int2 / 16 int8 / 8 fp16 values) are read
+// word by word or element by element.
+__device__ __forceinline__ uint4 canonical_piece(int fmt, const void* __restrict__ w, int64_t n, int64_t K,
+                                                 int64_t k0) {
+  const int pf = pack_factor(fmt);
+  const int per16 = pf == 1 ? (fmt == FMT_I8 ? 16 : 8) : 4 * pf;  // values per 16 bytes
+  const int64_t row_elems = pf == 1 ? K : K / pf;                  // elements (words) per row
+  const bool aligned = K % per16 == 0 && k0 + per16 <= K;
+  if (aligned) {
+    if (pf == 1) {
+      const size_t esz = fmt == FMT_I8 ? 1 : 2;
+      return *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(w) + ((size_t)n * K + k0) * esz);
+    }
+    return reinterpret_cast<const uint4*>(w)[((size_t)n * row_elems + k0 / pf) / 4];
+  }
+  union { uint32_t d[4]; uint8_t b[16]; uint16_t h[8]; uint4 u; } r;
+  r.u = make_uint4(0, 0, 0, 0);
+  if (pf > 1) {
+    const uint32_t* src = static_cast<const uint32_t*>(w) + (size_t)n * row_elems;
+    for (int t = 0; t < 4; ++t)
+      if (k0 + (int64_t)t * pf < K) r.d[t] = src[k0 / pf + t];  // K is a multiple of pf
+  } else if (fmt == FMT_I8) {
+    const uint8_t* src = static_cast<const uint8_t*>(w) + (size_t)n * K;
+    for (int e = 0; e < 16; ++e)
+      if (k0 + e < K) r.b[e] = src[k0 + e];
+  } else {
+    const uint16_t* src = static_cast<const uint16_t*>(w) + (size_t)n * K;
+    for (int e = 0; e < 8; ++e)
+      if (k0 + e < K) r.h[e] = src[k0 + e];
+  }
+  return r.u;
+}
 
 __global__ void pack_weights_kernel(int fmt, const void* __restrict__ w, uint4* __restrict__ out,
                                     int64_t N, int64_t K, int64_t NB, int64_t n_pieces) {
@@ -24,8 +61,8 @@ __global__ void pack_weights_kernel(int fmt, const void* __restrict__ w, uint4* 
     const int64_t k0 = kb * KB + (int64_t)kq * (KB / 4);
     uint4 r = make_uint4(0, 0, 0, 0);
     if (n < N) {
+      const uint4 src = canonical_piece(fmt, w, n, K, k0);
       if (fmt == FMT_I4 || fmt == FMT_U4) {
-        const uint4 src = reinterpret_cast<const uint4*>(w)[(n * (K / 8) + k0 / 8) / 4];
         const uint32_t in[4] = {src.x, src.y, src.z, src.w};
         uint32_t o[4];
         for (int t = 0; t < 4; ++t) {
@@ -39,7 +76,6 @@ __global__ void pack_weights_kernel(int fmt, const void* __restrict__ w, uint4* 
         }
         r = make_uint4(o[0], o[1], o[2], o[3]);
       } else if (fmt == FMT_I2) {
-        const uint4 src = reinterpret_cast<const uint4*>(w)[(n * (K / 16) + k0 / 16) / 4];
         const uint32_t in[4] = {src.x, src.y, src.z, src.w};
         uint32_t o[4];
         for (int t = 0; t < 4; ++t) {
@@ -54,25 +90,26 @@ __global__ void pack_weights_kernel(int fmt, const void* __restrict__ w, uint4* 
           o[t] = acc;
         }
         r = make_uint4(o[0], o[1], o[2], o[3]);
-      } else if (fmt == FMT_I8) {
-        r = reinterpret_cast<const uint4*>(static_cast<const int8_t*>(w) + n * K + k0)[0];
-      } else {  // FMT_F16
-        r = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + n * K + k0)[0];
+      } else {  // FMT_I8, FMT_F16: stored as they are
+        r = src;
       }
     }
     out[p] = r;
   }
 }
 
+// rows g >= G (groups wholly past K, whose positions read zero activations) get
+// zero scales and zero points
 __global__ void pack_scales_kernel(const uint16_t* __restrict__ s, const uint16_t* __restrict__ z,
-                                   void* __restrict__ out, int64_t N, int64_t Npad, int64_t G) {
-  const int64_t total = G * Npad;
+                                   void* __restrict__ out, int64_t N, int64_t Npad, int64_t G, int64_t G_store) {
+  const int64_t total = G_store * Npad;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t g = i / Npad, n = i - g * Npad;
-    const uint16_t sv = n < N ? s[n * G + g] : 0;
+    const bool in = n < N && g < G;
+    const uint16_t sv = in ? s[n * G + g] : 0;
     if (z) {
-      const uint16_t zv = n < N ? z[n * G + g] : 0;
+      const uint16_t zv = in ? z[n * G + g] : 0;
       static_cast<uint32_t*>(out)[i] = (uint32_t)sv | ((uint32_t)zv << 16);
     } else {
       static_cast<uint16_t*>(out)[i] = sv;
@@ -97,9 +134,9 @@ hipError_t launch_pack(const Layout& L, const void* w, const void* s, const void
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.G == 0) return e;
   void* sdst = static_cast<char*>(packed) + L.s_offset;
-  hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(L.G * L.Npad, 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(L.G_store * L.Npad, 256)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(s), L.zeros ? static_cast<const uint16_t*>(z) : nullptr,
-                     sdst, L.N, L.Npad, L.G);
+                     sdst, L.N, L.Npad, L.G, L.G_store);
   return hipGetLastError();
 }
 

@@ -53,14 +53,22 @@ constexpr int kb_of(int fmt) {
   return fmt == FMT_I2 ? 256 : fmt == FMT_I8 ? 64 : fmt == FMT_F16 ? 32 : 128;
 }
 
+// K is padded to whole superblocks (Kpad = roundup(K, KB)): the blob holds zero
+// codes at positions K .. Kpad - 1 and, where scale groups are smaller than a
+// superblock, zero scales for the groups past K (G_store rows in all), and runs
+// read activations zero-padded to Kpad, so those positions add exactly nothing.
 struct Layout {
   int fmt;
-  int64_t N, K, Npad, NB, nkb;
+  int64_t N, K, Kpad, Npad, NB, nkb;
   int32_t group_size;  // as given: 0, -1 or g > 0
-  int64_t G;           // number of scale groups (0 without scaling)
+  int64_t G;           // number of scale groups of the input table (0 without scaling)
+  int64_t G_store;     // scale rows in the blob (G, or more to cover Kpad)
   bool zeros;
   size_t w_bytes, s_offset, s_bytes, total;
 };
+
+// canonical weight values per 32-bit word (int8 / fp16 rows are plain arrays)
+constexpr int pack_factor(int fmt) { return fmt == FMT_I2 ? 16 : (fmt == FMT_I4 || fmt == FMT_U4) ? 8 : 1; }
 
 // Arguments of every compute kernel (GEMV and MFMA), passed by value.
 struct RunArgs {
@@ -140,6 +148,10 @@ void dl_tile_dims(int tile, int* bm, int* bn);
 int choose_dl_tile(int fmt, int64_t M, int64_t N, int k_parts, int smode);
 hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// dst[m, k] = k < K ? A[m, k] : 0 for rows of Kpad elements of esz bytes (Kpad * esz a
+// multiple of 16, dst 16-byte aligned; A any alignment of its element size)
+hipError_t launch_pad_rows(const void* A, void* dst, int64_t M, int64_t K, int64_t Kpad, int esz,
+                           hipStream_t st);
 // C[m, n] = bias[n] (int32) for the integer atomics to add into
 hipError_t launch_fill_bias(const RunArgs& a, hipStream_t st);
 // per-row symmetric int8 quantisation of fp16 activations (quant.hip)

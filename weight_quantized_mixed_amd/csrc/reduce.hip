@@ -48,6 +48,23 @@ __global__ void fill_bias_kernel(int* __restrict__ C, const int* __restrict__ bi
       C[(size_t)m * N + n] = bias[n];
 }
 
+// one 16-byte chunk of a padded row per thread, its elements read one by one (the
+// source rows need not be 16-byte aligned)
+template <typename T>
+__global__ void pad_rows_kernel(const T* __restrict__ A, uint4* __restrict__ dst, int64_t M, int64_t K,
+                                int64_t Kpad) {
+  constexpr int E = 16 / sizeof(T);
+  const int64_t chunks_row = Kpad / E, total = M * chunks_row;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / chunks_row, k0 = (i - m * chunks_row) * E;
+    union { T v[E]; uint4 u; } c;
+#pragma unroll
+    for (int e = 0; e < E; ++e) c.v[e] = k0 + e < K ? A[m * K + k0 + e] : (T)0;
+    dst[i] = c.u;
+  }
+}
+
 int grid_for(size_t items, int threads) {
   size_t b = (items + threads - 1) / threads;
   if (b > 8192) b = 8192;
@@ -63,6 +80,18 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   uint32_t* tail = reinterpret_cast<uint32_t*>(static_cast<char*>(p) + n16 * 16);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n16 ? n16 : 1, 256)), dim3(256), 0, st,
                      static_cast<uint4*>(p), n16, tail, n4tail);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(const void* A, void* dst, int64_t M, int64_t K, int64_t Kpad, int esz,
+                           hipStream_t st) {
+  const size_t chunks = (size_t)M * (size_t)(Kpad * esz / 16);
+  if (esz == 2)
+    hipLaunchKernelGGL(pad_rows_kernel<uint16_t>, dim3(grid_for(chunks, 256)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(A), static_cast<uint4*>(dst), M, K, Kpad);
+  else
+    hipLaunchKernelGGL(pad_rows_kernel<uint8_t>, dim3(grid_for(chunks, 256)), dim3(256), 0, st,
+                       static_cast<const uint8_t*>(A), static_cast<uint4*>(dst), M, K, Kpad);
   return hipGetLastError();
 }
 
