@@ -103,11 +103,13 @@ typedef enum {
  *   M, N, K       problem sizes, each >= 1.  K must be a multiple of the values
  *                 per canonical word: 8 (I4/U4), 16 (I2), 1 (I8/F16), and of
  *                 group_size when that is > 0, else QGEMM_ERR_UNSUPPORTED.  The
- *                 kernels work on whole blocks of 128 (I4/U4), 256 (I2), 64 (I8)
- *                 or 32 (F16) positions: when K is not a multiple of that depth,
+ *                 kernels work on whole granules of 128 (I4/U4, I8), 256 (I2) or
+ *                 64 (F16) positions: when K is not a multiple of the granule,
  *                 the blob is zero-padded and every run first copies A into the
  *                 workspace with its rows zero-padded (the workspace then also
- *                 holds M * roundup(K, depth) activation elements).
+ *                 holds M * roundup(K, granule) activation elements).  The
+ *                 activations, M * roundup(K, granule) elements, must stay below
+ *                 4 GiB, else QGEMM_ERR_UNSUPPORTED.
  *   group_size    0 = no scaling (with_scaling False), -1 = one group per output
  *                 column over all of K, g > 0 = groups of g along K.  Scaled
  *                 formats are I4/U4 only; g > 0 must divide K and be a multiple
@@ -117,8 +119,8 @@ typedef enum {
  *                 separate workgroups and reduced with fp32/int32 global atomics
  *                 (default) or by ordered partials and one summing pass
  *                 (QGEMM_DETERMINISTIC; see qgemm_run).  At most K / unit, where
- *                 unit = group_size when it is a multiple of the block depth
- *                 (and larger), else the block depth (K rounded up to it).
+ *                 unit = group_size when it is a multiple of 128 (and larger),
+ *                 else the granule (K rounded up to it).
  *   flags         0, or QGEMM_DETERMINISTIC and / or QGEMM_SPLIT_AUTO.
  *   packed_bytes  out: size of the packed blob for qgemm_pack_weights/qgemm_run.
  *   workspace_bytes out: size of the device workspace qgemm_run needs (0 if none).

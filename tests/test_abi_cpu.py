@@ -285,8 +285,11 @@ def test_noalloc_rejects_before_any_device_call():
     (dict(K=4128, group_size=96), 4224),                     # groups of 96: 44 scale rows stored
     (dict(K=8, group_size=0), 128),
     (dict(a_dtype="i8", w_dtype="i2", out_dtype="i32", accum_dtype="i32", group_size=0, K=4112), 4352),
-    (dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0, K=4100), 4160),
-    (dict(w_dtype="f16", group_size=0, K=4099), 4128),
+    # int8 / fp16: granules of two blocks (the matrix-core tiles stage 128-byte activation rows)
+    (dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0, K=4100), 4224),
+    (dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0, K=4160), 4224),
+    (dict(w_dtype="f16", group_size=0, K=4099), 4160),
+    (dict(w_dtype="f16", group_size=0, K=4128), 4160),
 ])
 def test_k_granularity_pads_to_whole_blocks(kw, Kpad):
     """K needs only whole canonical words and whole groups: the blob is padded to whole

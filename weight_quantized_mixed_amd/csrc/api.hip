@@ -56,7 +56,7 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
   L->fmt = fmt;
   L->N = N;
   L->K = K;
-  L->Kpad = round_up(K, kb_of(fmt));
+  L->Kpad = round_up(K, kgrain_of(fmt));
   L->Npad = round_up(N, 256);
   L->NB = L->Npad / 16;
   L->nkb = L->Kpad / kb_of(fmt);
@@ -386,15 +386,18 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   // K: whole canonical words (8 int4, 16 int2 values); the kernels run on K padded
   // to whole superblocks
   if (K % pack_factor(fmt) != 0) return QGEMM_ERR_UNSUPPORTED;
-  const int64_t Kpad = round_up(K, KB);
+  const int64_t Kpad = round_up(K, kgrain_of(fmt));
   if (Kpad > INT32_MAX) return QGEMM_ERR_UNSUPPORTED;
 
-  // kernels index the blob with 32-bit uint4 offsets
+  // kernels index the blob with 32-bit uint4 offsets and the activations with
+  // 32-bit byte offsets
   if ((N + 255) / 256 * 256 / 16 * (Kpad / KB) * 64 >= INT32_MAX) return QGEMM_ERR_UNSUPPORTED;
+  if ((uint64_t)M * (uint64_t)Kpad * (a_dtype == QGEMM_F16 ? 2u : 1u) >= ((uint64_t)1 << 32))
+    return QGEMM_ERR_UNSUPPORTED;
 
   // split unit: whole superblocks, and whole groups when groups are whole superblocks
   // (then K is a multiple of the group, so Kpad = K)
-  const int64_t unit = scale_mode(fmt, group_size) == SC_BLOCK && group_size > KB ? group_size : KB;
+  const int64_t unit = scale_mode(fmt, group_size) == SC_BLOCK && group_size > KB ? group_size : kgrain_of(fmt);
   const int64_t n_units = Kpad / unit;
   if (k_parts > n_units) return QGEMM_ERR_INVALID_ARG;
 

@@ -85,6 +85,20 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
       : "memory");
 }
 
+// The same load in its scalar-base form: 64-bit wave-uniform base in SGPRs plus a
+// 32-bit offset per lane, so no per-lane 64-bit address is formed.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
 // (x & m) | c in one VALU op (masks that are not inline constants go in registers)
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
   uint32_t r;
@@ -118,6 +132,7 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, T...>, F&&
 #ifndef QG_DL_MAXST
 #define QG_DL_MAXST 16
 #endif
+
 #ifndef QG_DL_IL
 #define QG_DL_IL 1
 #endif
@@ -147,7 +162,7 @@ struct Geo {
   static constexpr bool PACKED = FMT == FMT_I4 || FMT == FMT_U4 || FMT == FMT_I2;
   static constexpr int KB = kb_of(FMT);
   static constexpr int ESZ = FP ? 2 : 1;
-  static constexpr int SPOS = PACKED ? KB / 2 : KB;
+  static constexpr int SPOS = PACKED ? KB / 2 : (QG_DL_WIDE ? 2 * KB : KB);
   static constexpr int NSTEP = SPOS / (FP ? 32 : 64);  // MFMA steps per stage
   static constexpr int ROWB = SPOS * ESZ;              // activation bytes per row per stage
   static constexpr int BSB = SPOS * 1024 / KB;         // weight bytes per 16 columns per stage
@@ -168,10 +183,11 @@ struct Geo {
     return n;
   }
   static constexpr int NSTAGE = BM == 256 ? fit((FMT == FMT_F16 || FMT == FMT_I8) ? 4 : 3) : fit(QG_DL_MAXST);
+  static constexpr int SB_PER_STAGE = SPOS > KB ? SPOS / KB : 1;  // superblocks per stage (fp16 / int8)
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KiB slots");
   static_assert(NSTEP == 1 || NSTEP == 2, "one or two MFMA steps per stage");
   static_assert(ROWB == 64 || ROWB == 128, "activation row bytes");
-  static_assert(NSTAGE >= 3 * KS, "ring depth");
+  static_assert(NSTAGE >= 3 * KS || (KS == 1 && NSTAGE >= 2), "ring depth");
   static_assert(KS == 1 || ((KS == 2 || KS == 4) && PACKED), "K groups: 2 or 4, for the two-step int4 / int2 stages");
   static constexpr int RED = NW * WTM * WTN * 64;  // accumulator vectors of one K group
   static_assert((KS - 1) * RED * 16 <= NSTAGE * STAGE, "K-group reduction fits in the ring");
@@ -228,59 +244,99 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   const int m0 = (first_m + in_group % gsz) * BM, n0 = (in_group / gsz) * BN;
 
   // ---- stages of this k-part
-  constexpr int SPB = KB / SPOS;  // stages per superblock
+  // stages per split unit (a unit is a whole number of stages)
   int u0, u1;
   part_units(a, part, u0, u1);
-  const int s0 = u0 * a.unit_kb * SPB, s1 = u1 * a.unit_kb * SPB;  // global stage indices
+  const int s0 = u0 * a.unit_kb * KB / SPOS, s1 = u1 * a.unit_kb * KB / SPOS;  // global stage indices
   const int nst = s1 - s0;
 
   const uint8_t* __restrict__ Ab = static_cast<const uint8_t*>(a.A);
-  const size_t a_row_bytes = (size_t)a.K * ESZ;
+  const uint32_t a_row_bytes = (uint32_t)a.K * ESZ;  // the plan keeps M * K * ESZ below 4 GiB
   const uint8_t* __restrict__ Wb = reinterpret_cast<const uint8_t*>(a.W);
+  constexpr int bytes_per_scale = ZEROS ? 4 : 2;
 
   // This wave's 1 KiB slots of a stage: A slots i * NWT + wave < NS_A, then B
   // slots likewise; wave 0 also loads the scale slot.
   const int la = (NS_A - wave + NWT - 1) / NWT, lb = (NS_B - wave + NWT - 1) / NWT;
   const int my_loads = la + lb + ((SCALED && wave == 0) ? 1 : 0);
 
-  // Per-lane global source of each direct load (the stage-dependent part is added
-  // at issue time).  A: one slot covers 1024 / ROWB rows.
+  // Per-lane 32-bit offset of each direct load from its stage's source, which is
+  // wave-uniform (the loads take the scalar-base form: no per-lane address
+  // arithmetic per stage).  A: one slot covers 1024 / ROWB rows.
   constexpr int CPR = ROWB / 16;
-  int a_row_off[A_MAX];
-  int a_chunk[A_MAX];
+  uint32_t a_off[A_MAX];
 #pragma unroll
   for (int i = 0; i < A_MAX; ++i) {
     const int sl = min(i * NWT + wave, NS_A - 1);
     const int c16 = sl * 64 + lane;  // 16-byte slot in the stage's A area
     const int r = c16 / CPR, p = c16 % CPR;
-    a_row_off[i] = min(m0 + r, a.M - 1);
-    a_chunk[i] = swz<ROWB>(r, p);  // chunk whose data belongs at position p of row r
+    // chunk swz(r, p) of the row belongs at position p
+    a_off[i] = (uint32_t)min(m0 + r, a.M - 1) * a_row_bytes + (uint32_t)swz<ROWB>(r, p) * 16;
   }
   // B: byte o of the stage's weight area is column block o / BSB, byte o % BSB of
   // it (plus the half-superblock offset of the stage when BSB = 512)
-  int b_off[B_MAX];
+  uint32_t b_off[B_MAX];
 #pragma unroll
   for (int i = 0; i < B_MAX; ++i) {
     const int sl = min(i * NWT + wave, NS_B - 1);
     const int o = (sl * 64 + lane) * 16;
-    b_off[i] = ((n0 >> 4) + o / BSB) * 1024 + o % BSB;
+    if constexpr (BSB <= 1024) {
+      b_off[i] = ((n0 >> 4) + o / BSB) * 1024 + o % BSB;
+    } else {
+      // superblock o % BSB / 1024 of the stage: the next superblock row of the blob
+      const int w = o % BSB;
+      b_off[i] = ((n0 >> 4) + o / BSB) * 1024 + (w >> 10) * a.NB * 1024 + (w & 1023);
+    }
   }
+  // scales: (scale[, zero]) of columns n0 .. n0 + BN - 1, up to 1 KiB (lanes past
+  // the end re-read the last 16 bytes into the unused part of the slot)
+  const uint32_t s_off = (uint32_t)min(lane * 16, BN * bytes_per_scale - 16);
 
-  // where stage st of this part goes (ring slot st % NSTAGE) and comes from
+  // The next stage to issue: its ring slot and its wave-uniform sources.  Stages
+  // are issued in order, so each advances the previous one by constant strides;
+  // past the part's last stage the sources stay put (clamped copies that are
+  // never consumed).
   struct StageSrc {
-    uint32_t dst;   // LDS byte address of the slot
-    size_t apos;    // byte offset of the stage in an activation row
-    size_t sb_row;  // byte offset of the stage's weights in the blob (column block 0)
-    int grp;        // scale group
+    uint32_t dst;      // LDS byte address of the ring slot
+    const uint8_t* a;  // the stage's activation columns (row 0)
+    const uint8_t* w;  // the stage's weights (column block 0)
+    const uint8_t* s;  // the stage's scale row (column n0)
   };
-  auto stage_src = [&](int st) {
-    StageSrc r;
-    const int gs = s0 + min(st, nst - 1);  // clamped: stages past the end are never consumed
-    const int pos = gs * SPOS;
-    r.dst = lds_off(lds + (st % NSTAGE) * STAGE);
-    r.apos = (size_t)pos * ESZ;
-    r.sb_row = (size_t)(pos / KB) * a.NB * 1024 + (size_t)(pos % KB) * 1024 / KB;
-    r.grp = !SCALED ? 0 : a.g_shift >= 0 ? pos >> a.g_shift : pos / a.group_size;
+  const uint32_t lds0 = lds_off(lds), lds_end = lds0 + NSTAGE * STAGE;
+  StageSrc next;
+  int next_st = 0;    // part-relative index of `next`
+  int grp_left = 0;   // stages from `next` to the end of its scale group
+  {
+    const int64_t pos0 = (int64_t)s0 * SPOS;
+    next.dst = lds0;
+    next.a = Ab + pos0 * ESZ;
+    next.w = Wb + (pos0 / KB) * a.NB * 1024 + (pos0 % KB) * 1024 / KB;
+    next.s = nullptr;
+    if constexpr (SCALED) {
+      int64_t grp = 0;
+      grp_left = 1 << 30;  // one group over K
+      if (a.group_size > 0) {
+        grp = pos0 / a.group_size;
+        grp_left = (int)((a.group_size - pos0 % a.group_size) / SPOS);
+      }
+      next.s = static_cast<const uint8_t*>(a.S) + ((size_t)grp * a.Npad + n0) * bytes_per_scale;
+    }
+  }
+  auto take_stage = [&]() {
+    const StageSrc r = next;
+    next.dst = next.dst + STAGE == lds_end ? lds0 : next.dst + STAGE;
+    if (next_st < nst - 1) {
+      next.a += SPOS * ESZ;
+      if constexpr (BSB == 512) next.w += (next_st & 1) ? (size_t)a.NB * 1024 - 512 : (size_t)512;
+      else next.w += (size_t)G::SB_PER_STAGE * a.NB * 1024;
+      if constexpr (SCALED) {
+        if (--grp_left == 0) {
+          next.s += (size_t)a.Npad * bytes_per_scale;
+          grp_left = a.group_size / SPOS;
+        }
+      }
+    }
+    ++next_st;
     return r;
   };
   // this wave's direct load e of a stage: A slots, then B slots, then (wave 0) scales
@@ -288,22 +344,16 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   auto dma_one = [&](const StageSrc& sa, auto E) {
     constexpr int e = decltype(E)::value;
     if constexpr (e < A_MAX) {
-      if (NS_A % NWT == 0 || e < la)
-        dma16(Ab + (size_t)a_row_off[e] * a_row_bytes + sa.apos + a_chunk[e] * 16, sa.dst + (e * NWT + wave) * 1024);
+      if (NS_A % NWT == 0 || e < la) dma16s(sa.a, a_off[e], sa.dst + (e * NWT + wave) * 1024);
     } else if constexpr (e < A_MAX + B_MAX) {
       constexpr int i = e - A_MAX;
-      if (NS_B % NWT == 0 || i < lb) dma16(Wb + sa.sb_row + b_off[i], sa.dst + A_BYTES + (i * NWT + wave) * 1024);
+      if (NS_B % NWT == 0 || i < lb) dma16s(sa.w, b_off[i], sa.dst + A_BYTES + (i * NWT + wave) * 1024);
     } else if (wave == 0) {
-      // (scale[, zero]) of columns n0 .. n0 + BN - 1: up to 1 KiB (lanes past the
-      // end re-read the last 16 bytes into the unused part of the slot)
-      constexpr int bytes_per = ZEROS ? 4 : 2;
-      const int off = min(lane * 16, BN * bytes_per - 16);
-      const uint8_t* src = static_cast<const uint8_t*>(a.S) + ((size_t)sa.grp * a.Npad + n0) * bytes_per + off;
-      dma16(src, sa.dst + A_BYTES + B_BYTES);
+      dma16s(sa.s, s_off, sa.dst + A_BYTES + B_BYTES);
     }
   };
-  auto issue = [&](int st) {
-    const StageSrc sa = stage_src(st);
+  auto issue = [&]() {
+    const StageSrc sa = take_stage();
     static_for(std::make_integer_sequence<int, NDMA>{}, [&](auto E) { dma_one(sa, E); });
   };
 
@@ -331,10 +381,11 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   // clobber) instead of __syncthreads, whose fence would drain the loads still in
   // flight.
   auto sync_round = [&](int rn) {
+    (void)rn;  // its stages (rn * KS + NSTAGE - KS ..) are the next KS to issue
     wait_loads<G::LMIN, G::LMAX, NSTAGE - 2 * KS>(my_loads);
     asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-    for (int k = 0; k < KS; ++k) issue(rn * KS + NSTAGE - KS + k);
+    for (int k = 0; k < KS; ++k) issue();
   };
 
   // keeps the machine scheduler from moving instructions across it, so that the
@@ -349,7 +400,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
     constexpr int t = decltype(T)::value, i = decltype(I)::value;
     int chunk;
     if constexpr (PACKED) chunk = (q & 1) * 4 + (2 * t + (q >> 1));  // piece q & 1, word 2t + (q >> 1)
-    else chunk = q;                                                    // 8 fp16 / 16 int8 per lane group
+    else chunk = t * 4 + q;  // 8 fp16 / 16 int8 per lane group, four groups per step
     const int r = (wm * WTM + i) * 16 + l16;
     f.a[i] = *reinterpret_cast<const uint4*>(base + r * ROWB + swz<ROWB>(r, chunk) * 16);
   };
@@ -359,7 +410,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
     if constexpr (PACKED)
       rw[j] = *reinterpret_cast<const uint32_t*>(lb + ((q & 1) * 16 + l16) * 16 + (2 * t + (q >> 1)) * 4);
     else
-      f.b[j] = *reinterpret_cast<const uint4*>(lb + lane * 16);  // whole superblock, piece = lane
+      f.b[j] = *reinterpret_cast<const uint4*>(lb + t * 1024 + lane * 16);  // superblock t, piece = lane
     if constexpr (SCALED && t == 0) {
       const int col = (wn * WTN + j) * 16 + l16;
       if constexpr (ZEROS) {
@@ -453,7 +504,9 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   // the matrix core of its SIMD would idle.
   auto step_il = [&](const Frag& cur, Frag& nxt, const uint8_t* rb, auto T, auto DMA, int st_dma) {
     constexpr bool dma = decltype(DMA)::value;
-    const StageSrc sa = stage_src(dma ? st_dma : 0);
+    (void)st_dma;  // with DMA: stage st_dma, the next one to issue
+    StageSrc sa{};
+    if constexpr (dma) sa = take_stage();
     constexpr int UPW = ILP == 2 ? 1 : 4;  // upcast side ops per column block
     constexpr int ND = dma ? NDMA : 0, NU = PACKED ? UPW * WTN : 0;
     constexpr int NM = WTM * WTN;
@@ -505,7 +558,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
 
   // prologue: NSTAGE stages in flight, then the fragments of step 0
 #pragma unroll
-  for (int st = 0; st < NSTAGE; ++st) issue(st);
+  for (int st = 0; st < NSTAGE; ++st) issue();
   wait_loads<G::LMIN, G::LMAX, NSTAGE - KS>(my_loads);
   asm volatile("s_barrier" ::: "memory");
 
@@ -525,7 +578,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
       step_il(Y, X, slot(s + 2), I0{}, std::true_type{}, s + 1 + NSTAGE);
     }
     if (s < nst) compute(X, Y);
-  } else if constexpr (QG_DL_IL && ILP != 0 && KS == 1) {
+  } else if constexpr (QG_DL_IL && (ILP != 0 || !PACKED) && KS == 1) {
     // two steps per stage: step 0 reads step 1 of the same stage, step 1 follows
     // the barrier of the next stage and reads its step 0
     for (int s = 0; s < nst; ++s) {

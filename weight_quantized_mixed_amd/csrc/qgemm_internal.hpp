@@ -53,7 +53,20 @@ constexpr int kb_of(int fmt) {
   return fmt == FMT_I2 ? 256 : fmt == FMT_I8 ? 64 : fmt == FMT_F16 ? 32 : 128;
 }
 
-// K is padded to whole superblocks (Kpad = roundup(K, KB)): the blob holds zero
+// fp16 / int8 direct-load MFMA stages of two superblocks (128-byte activation rows;
+// 1) or one (64-byte rows; 0).  A direct load of 16 rows x 64 bytes moves half as
+// many bytes per clock as one of 8 rows x 128 bytes (a probe of global_load_lds_dwordx4
+// from L2 at a 32 KiB row stride: 70 against 143 bytes per ns per CU).
+#ifndef QG_DL_WIDE
+#define QG_DL_WIDE 1
+#endif
+// K granule of a format: K is padded to it and k-parts split at it (two superblocks
+// for fp16 / int8 with two-superblock stages, else one)
+constexpr int kgrain_of(int fmt) {
+  return (QG_DL_WIDE && (fmt == FMT_F16 || fmt == FMT_I8)) ? 2 * kb_of(fmt) : kb_of(fmt);
+}
+
+// K is padded to whole K granules (Kpad = roundup(K, kgrain_of)): the blob holds zero
 // codes at positions K .. Kpad - 1 and, where scale groups are smaller than a
 // superblock, zero scales for the groups past K (G_store rows in all), and runs
 // read activations zero-padded to Kpad, so those positions add exactly nothing.
