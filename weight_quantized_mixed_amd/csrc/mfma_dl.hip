@@ -132,6 +132,13 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, T...>, F&&
 #ifndef QG_DL_MAXST
 #define QG_DL_MAXST 16
 #endif
+// ring depth of the 256 x 256 tiles (fp16 / int8, packed formats), before the LDS fit
+#ifndef QG_DL_BIG_ST_F
+#define QG_DL_BIG_ST_F 4
+#endif
+#ifndef QG_DL_BIG_ST_P
+#define QG_DL_BIG_ST_P 3
+#endif
 
 #ifndef QG_DL_IL
 #define QG_DL_IL 1
@@ -182,7 +189,9 @@ struct Geo {
     while (n > 2 && (n * STAGE > 160 * 1024 || (n - KS) * LMAX > 63 || n % KS != 0)) --n;
     return n;
   }
-  static constexpr int NSTAGE = BM == 256 ? fit((FMT == FMT_F16 || FMT == FMT_I8) ? 4 : 3) : fit(QG_DL_MAXST);
+  static constexpr int cap(int n) { return n > 3 * KS ? n : 3 * KS; }
+  static constexpr int NSTAGE = BM == 256 ? fit((FMT == FMT_F16 || FMT == FMT_I8) ? QG_DL_BIG_ST_F : QG_DL_BIG_ST_P)
+                                          : fit(cap(QG_DL_MAXST));
   static constexpr int SB_PER_STAGE = SPOS > KB ? SPOS / KB : 1;  // superblocks per stage (fp16 / int8)
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KiB slots");
   static_assert(NSTEP == 1 || NSTEP == 2, "one or two MFMA steps per stage");
@@ -672,8 +681,14 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
 
 // the tile configurations: rows x columns; waves rows x columns x K groups.  Up
 // to 128 rows the waves never split the rows, so every weight fragment is
-// upcast once per workgroup; int4 / int2 (P) take K groups on the smaller tiles,
-// fp16 / int8 (F) split the columns only.
+// upcast once per workgroup; int4 / int2 (P) take K groups on the smaller tiles
+// and on 128 x 256, fp16 / int8 (F) split the columns (and the rows of 128 x 256).
+// Measured against the alternatives at N = K = 16384: fp16 / int8 64 x 128 with 8
+// waves instead of 4 (int8 M = 128 73.1 -> 64.3 us, fp16 133 -> 122 us); 128 x 256
+// as 2 x 4 waves for fp16 / int8 (M = 512: int8 139 -> 134 us, fp16 267 -> 256 us,
+// while int4 went 283 -> 324 us) and 1 x 4 x 2 for int4 / int2 (int4 283 -> 265 us);
+// int4 64 x 128 as 1 x 4 x 2 or 1 x 2 x 2 (no register spill) ran M = 128 in
+// 121 / 119 against 108 us.
 #ifndef QG_DL_WAVES_P_32x64
 #define QG_DL_WAVES_P_32x64 1, 2, 4
 #endif
@@ -696,7 +711,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
 #define QG_DL_WAVES_P_64x128 1, 2, 4
 #endif
 #ifndef QG_DL_WAVES_F_64x128
-#define QG_DL_WAVES_F_64x128 1, 4, 1
+#define QG_DL_WAVES_F_64x128 1, 8, 1
 #endif
 #ifndef QG_DL_WAVES_P_64x256
 #define QG_DL_WAVES_P_64x256 1, 4, 2
@@ -711,10 +726,10 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
 #define QG_DL_WAVES_F_128x128 1, 4, 1
 #endif
 #ifndef QG_DL_WAVES_P_128x256
-#define QG_DL_WAVES_P_128x256 1, 8, 1
+#define QG_DL_WAVES_P_128x256 1, 4, 2
 #endif
 #ifndef QG_DL_WAVES_F_128x256
-#define QG_DL_WAVES_F_128x256 1, 8, 1
+#define QG_DL_WAVES_F_128x256 2, 4, 1
 #endif
 #ifndef QG_DL_WAVES_P_256x256
 #define QG_DL_WAVES_P_256x256 2, 4, 1
