@@ -151,6 +151,11 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, T...>, F&&
 #ifndef QG_DL_IL_P_BIG
 #define QG_DL_IL_P_BIG 0
 #endif
+// int2 256 x 256: word by word (W2A8 16384^3 3620 -> 3289 us; int4 stays in runs,
+// 8152 against 8228 us)
+#ifndef QG_DL_IL_P_BIG_I2
+#define QG_DL_IL_P_BIG_I2 1
+#endif
 // share (percent) of a step's MFMAs that the side ops are spread over, and
 // whether the fragment reads go before the direct loads (1) or after (0)
 #ifndef QG_DL_IL_SPAN
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   constexpr int SPOS = G::SPOS, ROWB = G::ROWB, BSB = G::BSB, NSTAGE = G::NSTAGE, NSTEP = G::NSTEP;
   constexpr int KB = G::KB, ESZ = G::ESZ;
   constexpr int A_BYTES = G::A_BYTES, B_BYTES = G::B_BYTES, STAGE = G::STAGE;
-  constexpr int ILP = BM == 256 ? QG_DL_IL_P_BIG : QG_DL_IL_P;  // measured per tile height
+  constexpr int ILP = BM == 256 ? (FMT == FMT_I2 ? QG_DL_IL_P_BIG_I2 : QG_DL_IL_P_BIG) : QG_DL_IL_P;  // measured
   constexpr int NS_A = G::NS_A, NS_B = G::NS_B, A_MAX = G::A_MAX, B_MAX = G::B_MAX;
   typedef typename std::conditional<FP, float4v, int4v>::type acc_v;
 
