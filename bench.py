@@ -383,6 +383,9 @@ def main():
     ap.add_argument("--exact", action="store_true", help="--only names one grid entry exactly")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales HBM counters)")
+    ap.add_argument("--torch-matmul", type=int, default=0, metavar="S",
+                    help="only time torch.matmul (the vendor BLAS) on fp16 S x S x S, the weight stored "
+                         "[N, K] as here, as a comparison for the dense fp16 rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path does not "
@@ -403,6 +406,29 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}))
+        return
+
+    if args.torch_matmul:
+        S = args.torch_matmul
+        g = torch.Generator(device="cuda").manual_seed(1)
+        A = torch.randn((S, S), dtype=torch.float16, device="cuda", generator=g)
+        W = torch.randn((S, S), dtype=torch.float16, device="cuda", generator=g)   # [N, K]
+        Wt = W.t()   # a K-major view of the [N, K] weight, as qgemm stores it
+        for _ in range(3):
+            torch.matmul(A, Wt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(5):
+            e0.record()
+            torch.matmul(A, Wt)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = sorted(ts)[len(ts) // 2]
+        print(json.dumps({"torch_matmul_fp16": S, "us": round(t * 1e6, 1),
+                          "tflops": round(2.0 * S ** 3 / t / 1e12, 1),
+                          "frac_of_2.5PF": round(2.0 * S ** 3 / t / PEAK["f16"], 4)}))
         return
 
     head = HEADLINE

@@ -108,14 +108,20 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 
 // position (in 16-byte units) of chunk c of activation row r.  Only r mod 16
 // enters, so rows that are 16 apart share one pattern and a fragment read's lane
-// addresses differ between sub-tiles by a constant offset; any 16 consecutive
-// rows reading one chunk spread over distinct 16-byte bank groups.
-template <int ROWB>
+// addresses differ between sub-tiles by a constant offset.  A fragment read
+// (ds_read_b128) has lanes 16 q + j read row j at chunk c(q): chunks 4 t + q for
+// fp16 / int8, (q & 1) * 4 + 2 t + (q >> 1) for the packed formats.  The patterns
+// keep every 16 lanes on distinct 16-byte slots of 256 bytes, every 32 lanes on
+// distinct slots of 512 bytes and all 64 on distinct slots of 1 KiB (the LDS of
+// gfx950 serves a 16-byte read in passes of 32 lanes: with rows 128 bytes long an
+// XOR by (r ^ r >> 3) & 7, distinct only per 16 lanes, stalled the fp16 16384^3
+// product on bank conflicts for 17 % of its cycles).
+template <int ROWB, bool PACKED>
 __device__ __forceinline__ int swz(int r, int c) {
   r &= 15;
   if constexpr (ROWB == 64) return c ^ (((r >> 1) ^ (r >> 2)) & 3);
-  else if constexpr (ROWB == 128) return c ^ ((r ^ (r >> 3)) & 7);
-  else return c ^ r;
+  else if constexpr (PACKED) return c ^ (((r >> 2) & 3) | (((r >> 1) & 1) << 2));
+  else return c ^ ((r >> 1) & 7);
 }
 
 template <int... T, typename F>
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
     const int c16 = sl * 64 + lane;  // 16-byte slot in the stage's A area
     const int r = c16 / CPR, p = c16 % CPR;
     // chunk swz(r, p) of the row belongs at position p
-    a_off[i] = (uint32_t)min(m0 + r, a.M - 1) * a_row_bytes + (uint32_t)swz<ROWB>(r, p) * 16;
+    a_off[i] = (uint32_t)min(m0 + r, a.M - 1) * a_row_bytes + (uint32_t)swz<ROWB, PACKED>(r, p) * 16;
   }
   // B: byte o of the stage's weight area is column block o / BSB, byte o % BSB of
   // it (plus the half-superblock offset of the stage when BSB = 512)
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
     if constexpr (PACKED) chunk = (q & 1) * 4 + (2 * t + (q >> 1));  // piece q & 1, word 2t + (q >> 1)
     else chunk = t * 4 + q;  // 8 fp16 / 16 int8 per lane group, four groups per step
     const int r = (wm * WTM + i) * 16 + l16;
-    f.a[i] = *reinterpret_cast<const uint4*>(base + r * ROWB + swz<ROWB>(r, chunk) * 16);
+    f.a[i] = *reinterpret_cast<const uint4*>(base + r * ROWB + swz<ROWB, PACKED>(r, chunk) * 16);
   };
   auto read_b = [&](Frag& f, const uint8_t* base, auto T, auto J) {
     constexpr int t = decltype(T)::value, j = decltype(J)::value;
