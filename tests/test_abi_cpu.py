@@ -316,3 +316,20 @@ def test_k_granularity_pads_to_whole_blocks(kw, Kpad):
         assert wb == -(-acc // 256) * 256 + M * Kpad * (1 if kw.get("a_dtype") == "i8" else 2)
     finally:
         q.qgemm_destroy(plan)
+
+
+def test_library_splits_long_int4_tiles_itself():
+    """k_parts 1 with int4 / uint4, 33..256 rows, N >= 4096, K >= 8192: two parts summed
+    in order, so the plan reports a workspace of two fp32 partials; elsewhere none."""
+    for kw, wb_expect in [
+        (dict(M=128, N=16384, K=16384), 2 * 128 * 16384 * 4),
+        (dict(M=256, N=4096, K=11008, group_size=-1, w_dtype="u4", has_zeros=1), 2 * 256 * 4096 * 4),
+        (dict(M=32, N=16384, K=16384), 0),                     # skinny: matrix-core GEMV
+        (dict(M=512, N=16384, K=16384), 0),                    # enough tiles
+        (dict(M=128, N=16384, K=4096), 0),                     # short K
+        (dict(M=128, N=2048, K=16384), 0),                     # narrow
+        (dict(M=128, N=16384, K=16384, w_dtype="f16", group_size=0), 0),
+    ]:
+        plan, _, wb = _create(**kw)
+        q.qgemm_destroy(plan)
+        assert wb == wb_expect, kw

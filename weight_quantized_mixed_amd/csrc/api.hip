@@ -32,6 +32,7 @@ struct qgemm_plan {
   qg_choice ch;      // kernels for M rows (calls with fewer rows choose again)
   int32_t unit_kb, n_units;
   bool two_pass;     // split-K reduced by partials + one ordered pass (else atomics)
+  int32_t auto_parts;  // k_parts 1: parts the library splits K into on its own for M > 32 (0: none)
   size_t ws_bytes;
 };
 
@@ -113,14 +114,14 @@ qgemm_status fill_layout(Layout* L, int fmt, int64_t N, int64_t K, int32_t g, bo
 #ifndef QG_GEMV_NARROW_BELOW
 #define QG_GEMV_NARROW_BELOW 128
 #endif
-bool choose_gemv_narrow(const qgemm_plan* p, int64_t M) {
-  return M == 1 && (p->N + 63) / 64 * p->k_parts < QG_GEMV_NARROW_BELOW;
+bool choose_gemv_narrow(const qgemm_plan* p, int64_t M, int kp) {
+  return M == 1 && (p->N + 63) / 64 * kp < QG_GEMV_NARROW_BELOW;
 }
 
-int choose_gemv_waves(const qgemm_plan* p, int cols) {
+int choose_gemv_waves(const qgemm_plan* p, int cols, int kp) {
   const int64_t rb = (p->N + cols - 1) / cols;
-  const int64_t per_part = p->L.nkb / p->k_parts;
-  int64_t want = (QG_GEMV_TARGET_WAVES + rb * p->k_parts - 1) / (rb * p->k_parts);
+  const int64_t per_part = p->L.nkb / kp;
+  int64_t want = (QG_GEMV_TARGET_WAVES + rb * kp - 1) / (rb * kp);
   int64_t maxw = per_part / 2;
   if (maxw < 1) maxw = 1;
   if (maxw > GEMV_MAX_WAVES) maxw = GEMV_MAX_WAVES;
@@ -133,9 +134,9 @@ int choose_gemv_waves(const qgemm_plan* p, int cols) {
 // activation load) whose workgroups still occupy 60 % of the 256 CUs, else 1.  N =
 // 4096 thus runs 256 workgroups of 16 columns instead of 64 of 64: W4A16 M = 8,
 // K = 11008 in 10.0 against 16.4 us, fp16 M = 8, K = 4096 in 8.1 against 14.1 us.
-int choose_gemv_cb(const qgemm_plan* p) {
+int choose_gemv_cb(const qgemm_plan* p, int kp) {
   for (int cb : {4, 2}) {
-    const int64_t wgs = (p->N + 16 * cb - 1) / (16 * cb) * p->k_parts;
+    const int64_t wgs = (p->N + 16 * cb - 1) / (16 * cb) * kp;
     const int64_t waves = (wgs + 255) / 256;
     if (wgs * 10 >= waves * 256 * 6) return cb;
   }
@@ -143,12 +144,12 @@ int choose_gemv_cb(const qgemm_plan* p) {
 }
 
 // LDS-staged kernel: largest tile that still gives every CU a workgroup (256 CUs).
-int choose_tile(const qgemm_plan* p, int64_t M) {
+int choose_tile(const qgemm_plan* p, int64_t M, int kp) {
   if (M <= 32) return TILE_32x64;
   auto wgs = [&](int tile) {
     int bm, bn;
     tile_dims(p->L.fmt, tile, &bm, &bn);
-    return ((M + bm - 1) / bm) * ((p->N + bn - 1) / bn) * p->k_parts;
+    return ((M + bm - 1) / bm) * ((p->N + bn - 1) / bn) * kp;
   };
   if (M >= 256 && wgs(TILE_BIG) >= 256) return TILE_BIG;
   return wgs(TILE_128x128) >= 256 ? TILE_128x128 : TILE_64x64;
@@ -189,25 +190,52 @@ bool two_pass_split(int64_t M, size_t partial_bytes, bool out_f16, uint32_t flag
   return out_f16 || M >= QG_TWO_PASS_INT_MIN_M;
 }
 
+// k-parts and reduction of a run of M rows: the plan's, or the library's own split
+// (ordered partials) for the shapes it applies to
+struct qg_split {
+  int kp;
+  bool two_pass;
+};
+qg_split split_of(const qgemm_plan* p, int64_t M) {
+  if (p->auto_parts > 1 && M > 32) return {p->auto_parts, true};
+  return {p->k_parts, p->two_pass};
+}
+
+// The library's own K split (plans of k_parts 1): int4 / uint4 with 33 to 256 rows,
+// N from 4096 and K from 8192, where the tiles that fill the CUs are few and long: two parts
+// summed in part order (bitwise reproducible).  N = K = 16384, M = 128: 109 -> 91 us
+// (128 x 128 tiles over both parts instead of 64 x 128); N = 4096, K = 11008: 51 ->
+// 40 us.  fp16 and int8 ran slower split (122 / 68 against 120 / 64 us).
+#ifndef QG_AUTO_SPLIT
+#define QG_AUTO_SPLIT 1
+#endif
+int auto_parts_of(int fmt, int64_t M, int64_t N, int64_t Kpad, int k_parts, int64_t n_units) {
+  if (!QG_AUTO_SPLIT || k_parts != 1 || n_units < 2) return 0;
+  if (fmt != FMT_I4 && fmt != FMT_U4) return 0;
+  if (M <= 32 || M > 256 || Kpad < 8192 || N < 4096) return 0;
+  return 2;
+}
+
 qg_choice choose(const qgemm_plan* p, int64_t M) {
+  const int kp = split_of(p, M).kp;
   qg_choice c;
   c.path = M <= 8 ? QGEMM_PATH_GEMV : QGEMM_PATH_MFMA;
-  c.tile = choose_tile(p, M);
-  c.dl_tile = c.path == QGEMM_PATH_MFMA ? choose_dl_tile(p->L.fmt, M, p->N, p->k_parts,
+  c.tile = choose_tile(p, M, kp);
+  c.dl_tile = c.path == QGEMM_PATH_MFMA ? choose_dl_tile(p->L.fmt, M, p->N, kp,
                                                           scale_mode(p->L.fmt, p->group_size))
                                         : -1;
-  c.gemv_narrow = c.path == QGEMM_PATH_GEMV && choose_gemv_narrow(p, M);
+  c.gemv_narrow = c.path == QGEMM_PATH_GEMV && choose_gemv_narrow(p, M, kp);
   c.gemv_mfma = !c.gemv_narrow && M >= QG_GEMV_MFMA_MIN_M && M <= QG_GEMV_MFMA_MAX_M &&
                 ((QG_GEMV_MFMA_FMTS >> p->L.fmt) & 1);
   const int smode = scale_mode(p->L.fmt, p->group_size);
   // two rows as well when the matrix is narrow enough for 16- or 32-column
   // workgroups, which the dot-product GEMV does not have (N = 4096: 4.8 against
   // 7.8 us at K = 4096, 8.4 against 16.0 us at K = 11008)
-  const int min_m4 = choose_gemv_cb(p) < 4 ? 2 : QG_GEMV4_MFMA_MIN_M;
+  const int min_m4 = choose_gemv_cb(p, kp) < 4 ? 2 : QG_GEMV4_MFMA_MIN_M;
   c.gemv_mfma4 = (p->L.fmt == FMT_I4 || p->L.fmt == FMT_U4) && !c.gemv_narrow && smode != SC_PIECE &&
                  M >= min_m4 && M <= (smode == SC_NONE ? QG_GEMV4_MFMA_MAX_M_UNSCALED : QG_GEMV4_MFMA_MAX_M);
-  c.gemv_cb = (c.gemv_mfma || c.gemv_mfma4) ? choose_gemv_cb(p) : 4;
-  c.gemv_waves = choose_gemv_waves(p, c.gemv_narrow ? 16 : (c.gemv_mfma || c.gemv_mfma4) ? 16 * c.gemv_cb : 64);
+  c.gemv_cb = (c.gemv_mfma || c.gemv_mfma4) ? choose_gemv_cb(p, kp) : 4;
+  c.gemv_waves = choose_gemv_waves(p, c.gemv_narrow ? 16 : (c.gemv_mfma || c.gemv_mfma4) ? 16 * c.gemv_cb : 64, kp);
   return c;
 }
 
@@ -237,13 +265,14 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
   if (p->group_size < 0) a.g_shift = 31;
   else if (p->group_size > 0 && (p->group_size & (p->group_size - 1)) == 0) a.g_shift = __builtin_ctz(p->group_size);
   a.zeros = p->has_zeros;
-  a.k_parts = p->k_parts;
+  const qg_split sp = split_of(p, M);
+  a.k_parts = sp.kp;
   a.unit_kb = p->unit_kb;
   a.n_units = p->n_units;
   a.waves = ch.gemv_waves;
   a.gemv_cb = ch.gemv_cb;
   a.sb_per_group = p->group_size > KB ? p->group_size / KB : p->group_size < 0 ? (int32_t)p->L.nkb : 1;
-  a.out_mode = p->k_parts == 1 ? OUT_STORE : p->two_pass ? OUT_PARTIAL : OUT_ATOMIC;
+  a.out_mode = sp.kp == 1 ? OUT_STORE : sp.two_pass ? OUT_PARTIAL : OUT_ATOMIC;
   return a;
 }
 
@@ -255,9 +284,10 @@ namespace {
 // split-K accumulator or partials, then (K not a multiple of the superblock depth)
 // the activations zero-padded to Kpad, 256-byte aligned
 size_t split_ws_bytes(const qgemm_plan* p, int64_t M) {
-  if (p->k_parts == 1) return 0;
+  const qg_split sp = split_of(p, M);
+  if (sp.kp == 1) return 0;
   const size_t mn4 = (size_t)M * (size_t)p->N * 4;
-  if (p->two_pass) return mn4 * (size_t)p->k_parts;
+  if (sp.two_pass) return mn4 * (size_t)sp.kp;
   return p->out_dtype == QGEMM_F16 ? mn4 : 0;
 }
 size_t a_esz(const qgemm_plan* p) { return p->a_dtype == QGEMM_F16 ? 2 : 1; }
@@ -417,9 +447,10 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   fill_layout(&p->L, fmt, N, K, group_size, has_zeros != 0);
   p->unit_kb = (int32_t)(unit / KB);
   p->n_units = (int32_t)n_units;
-  p->ch = choose(p, M);
+  p->auto_parts = auto_parts_of(fmt, M, N, Kpad, k_parts, n_units);
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   p->two_pass = k_parts > 1 && two_pass_split(M, mn4 * (size_t)k_parts, out_dtype == QGEMM_F16, flags);
+  p->ch = choose(p, M);
   p->ws_bytes = run_ws_bytes(p, M);  // int32 output with atomics: none (straight into C)
   if (packed_bytes) *packed_bytes = p->L.total;
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
