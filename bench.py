@@ -294,6 +294,8 @@ GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128
         + [{"w": w, "M": M, "N": 16384, "K": 16384, "dq": True, "bias": True} for w in ("i8", "i2")
            for M in (1, 512)]
         + [{"w": "quant", "M": M, "K": 16384} for M in (512, 16384)]
+        # the per-call floor: the smallest product (one 16 x 128 weight block), one kernel
+        + [{"w": "i4", "M": 1, "N": 16, "K": 128, "g": 128}]
         + [{"w": "f16", "M": 16384, "N": 16384, "K": 16384},
            {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}])
 
