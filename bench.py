@@ -14,7 +14,9 @@ Prints ONE JSON line: value = achieved algorithmic HBM bandwidth of the
 workload (GB/s); `roofline` for its kernel; `grid` with the µs, TFLOP/s or
 TOP/s, GB/s and roofline fraction of every other configuration of the grid
 (M = 1..16384 at N = K = 16384, and the LLaMA-7B projection shapes of hidet
-issue #364); `cpu_baseline` = the CPU oracle on the same workload.
+issue #364), each with the CPU oracle's single-thread time for the same call
+(`cpu_us`, extrapolated from a 64-column sample); `cpu_baseline` = the CPU
+oracle on the headline workload; `targets` (last) = the rows with stated targets.
 """
 from __future__ import annotations
 
@@ -372,6 +374,35 @@ def targets(out):
     return t
 
 
+def oracle_us(c):
+    """Single-thread time of the CPU oracle for one call of a grid entry, extrapolated from
+    a sample: all K, 64 output columns, and all rows up to 64 (else 64): the oracle's
+    cost grows with the columns it unpacks and with rows x columns of its product."""
+    import numpy as np
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_limits
+    M, K = c["M"], c["K"]
+    Ms = min(M, 64)
+    with threadpool_limits(limits=1):
+        if c["w"] == "quant":
+            A = synth.draw_fp16_activations(Ms, K, seed=1)
+            t0 = time.perf_counter()
+            oracle.quantize_rows(A)
+            return round((time.perf_counter() - t0) * 1e6 * M / Ms, 1)
+        N = c["N"]
+        Ns = min(N, 64)
+        g = c.get("g", 0) if c["w"] in ("i4", "u4") else 0
+        p = synth.make_problem(Ms, Ns, K, c["w"], group_size=g, has_zeros=c.get("zeros", False), seed=1)
+        t0 = time.perf_counter()
+        if c.get("dq"):
+            oracle.qgemm_ref_scaled(p.A, p.w, N=Ns, K=K, w_dtype=p.w_dtype,
+                                    row_scales=np.ones(Ms, np.float32), col_scales=np.ones(Ns, np.float32))
+        else:
+            oracle.qgemm_ref(p.A, p.w, p.s, p.z, N=Ns, K=K, w_dtype=p.w_dtype, group_size=p.group_size)
+        return round((time.perf_counter() - t0) * 1e6 * (N / Ns) * (M / Ms), 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -468,6 +499,8 @@ def main():
             b = make_bench(c, synth.seed_for(6, i))
             grid.append(measure_grid_entry(b))
             r = grid[-1]
+            if not args.no_cpu:
+                r["cpu_us"] = oracle_us(c)
             print(f"[bench] {r['c']}: {r['us']} us, {r['frac']}", file=sys.stderr, flush=True)
             b.close()
             del b

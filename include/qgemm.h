@@ -201,9 +201,11 @@ qgemm_status qgemm_run_ex(const qgemm_plan* plan, int64_t M, const void* A, cons
  * that forbid hipMalloc).  Split-K runs in a fixed scratch array inside the
  * library, one per GPU, of QGEMM_NOALLOC_MAX_SCRATCH bytes, which each GPU the
  * library runs on holds until the process ends; this call itself allocates
- * nothing.  It needs run-time M * N * 4 bytes of scratch for atomic split-K with
- * fp16 output, k_parts * M * N * 4 for the two-pass reduction, none otherwise;
- * more than the maximum returns QGEMM_ERR_UNSUPPORTED before any device call.
+ * nothing.  It needs the workspace that qgemm_run_ex would for run-time M (the
+ * atomic accumulator or the two-pass partials, plus the zero-padded activation
+ * rows when K is not a whole number of blocks; none for an unsplit plan of
+ * whole blocks); more than the maximum returns QGEMM_ERR_UNSUPPORTED before
+ * any device call.
  * Every call on one GPU shares that GPU's scratch: calls that may overlap in
  * time on one GPU (other streams, other threads) race and must be serialised by
  * the caller.  The stream must belong to the current device.  Plans with
