@@ -86,17 +86,11 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 }
 
 // The same load in its scalar-base form: 64-bit wave-uniform base in SGPRs plus a
-// 32-bit offset per lane, so no per-lane 64-bit address is formed.
+// 32-bit offset per lane, so no per-lane 64-bit address is formed.  The LDS base
+// is an operand bound to m0, so the compiler writes m0 once per load and knows it
+// holds the value (no save and restore around the load).
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_base)
-      : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds_base) : "memory");
 }
 
 // (x & m) | c in one VALU op (masks that are not inline constants go in registers)
