@@ -298,8 +298,12 @@ GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128
         + [{"w": "quant", "M": M, "K": 16384} for M in (512, 16384)]
         # the per-call floor: the smallest product (one 16 x 128 weight block), one kernel
         + [{"w": "i4", "M": 1, "N": 16, "K": 128, "g": 128}]
+        # M = N = K = 16384: the pages' five large-M products (fp16, int4 unscaled and with
+        # one group over K, W8A8, W2A8) and uint4 with g = 128 zero points
         + [{"w": "f16", "M": 16384, "N": 16384, "K": 16384},
-           {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}])
+           {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}]
+        + [{"w": "i4", "M": 16384, "N": 16384, "K": 16384, "g": g} for g in (0, -1)]
+        + [{"w": w, "M": 16384, "N": 16384, "K": 16384} for w in ("i8", "i2")])
 
 
 # the timed workload: W4A16 decode at M = 1, N = K = 16384, g = 128, k_parts = 1
