@@ -125,9 +125,11 @@ typedef enum {
  *   packed_bytes  out: size of the packed blob for qgemm_pack_weights/qgemm_run.
  *   workspace_bytes out: size of the device workspace qgemm_run needs (0 if none).
  *                 A plan of k_parts 1 may need one too: for I4 / U4 weights with
- *                 33 to 256 rows, N >= 4096 and K >= 8192 the library splits K in
- *                 two itself (runs of more than 32 rows) and sums the two partial
- *                 products in a fixed order, so results stay bitwise reproducible.
+ *                 33 to 256 rows, N >= 4096 and K >= 8192 the library splits K
+ *                 itself (runs of more than 32 rows) into 2, 4 or 8 parts (as many as
+ *                 one wave of 256 workgroups of 128 x 128 output tiles takes) and sums
+ *                 the partial products in a fixed order, so results stay bitwise
+ *                 reproducible; the workspace holds those parts' fp32 partials.
  */
 qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K,
                           qgemm_dtype a_dtype, qgemm_dtype w_dtype, qgemm_dtype out_dtype,

@@ -319,11 +319,16 @@ def test_k_granularity_pads_to_whole_blocks(kw, Kpad):
 
 
 def test_library_splits_long_int4_tiles_itself():
-    """k_parts 1 with int4 / uint4, 33..256 rows, N >= 4096, K >= 8192: two parts summed
-    in order, so the plan reports a workspace of two fp32 partials; elsewhere none."""
+    """k_parts 1 with int4 / uint4, 33..256 rows, N >= 4096, K >= 8192: 2, 4 or 8 parts
+    (enough for 256 workgroups of 128 x 128 tiles) summed in order, so the plan reports a
+    workspace of that many fp32 partials; elsewhere none."""
     for kw, wb_expect in [
         (dict(M=128, N=16384, K=16384), 2 * 128 * 16384 * 4),
-        (dict(M=256, N=4096, K=11008, group_size=-1, w_dtype="u4", has_zeros=1), 2 * 256 * 4096 * 4),
+        (dict(M=256, N=16384, K=8192), 2 * 256 * 16384 * 4),   # 256 tiles: still two
+        (dict(M=128, N=8192, K=8192), 4 * 128 * 8192 * 4),     # 64 tiles: four
+        (dict(M=128, N=4096, K=11008), 8 * 128 * 4096 * 4),    # 32 tiles: eight
+        (dict(M=40, N=4096, K=8192), 8 * 40 * 4096 * 4),
+        (dict(M=256, N=4096, K=11008, group_size=-1, w_dtype="u4", has_zeros=1), 4 * 256 * 4096 * 4),
         (dict(M=32, N=16384, K=16384), 0),                     # skinny: matrix-core GEMV
         (dict(M=512, N=16384, K=16384), 0),                    # enough tiles
         (dict(M=128, N=16384, K=4096), 0),                     # short K

@@ -359,13 +359,14 @@ def test_k_tail_with_fewer_rows_and_bias(w_dtype, g, zeros, kp):
 @pytest.mark.parametrize("M,w_dtype,g,zeros", [(33, "i4", 128, False), (128, "u4", 128, True),
                                                (256, "i4", -1, False), (100, "u4", 0, False)])
 def test_library_k_split_reproducible(M, w_dtype, g, zeros):
-    """Plans of k_parts 1 that the library splits in two itself (int4 / uint4, 33..256
-    rows, N >= 4096, K >= 8192): oracle parity, bitwise-identical repeats, and run-time
-    row counts on both sides of the split (32 rows and fewer run unsplit)."""
+    """Plans of k_parts 1 that the library splits itself (int4 / uint4, 33..256 rows,
+    N >= 4096, K >= 8192; at N = 4096 eight parts up to 128 rows, four above): oracle
+    parity, bitwise-identical repeats, and run-time row counts on both sides of the split
+    (32 rows and fewer run unsplit)."""
     N, K = 4096, 8192
     say(f"library split M={M} {w_dtype} g={g} zeros={zeros}")
     c = Case(M, N, K, w_dtype, g, zeros, seed=4400 + M)
-    assert c.q.ws_bytes == 2 * M * N * 4
+    assert c.q.ws_bytes == (8 if M <= 128 else 4) * M * N * 4
     first = c.run()
     assert_matches(first, c.reference(), f"library split M={M}")
     for _ in range(3):

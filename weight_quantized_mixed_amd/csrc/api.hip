@@ -202,10 +202,12 @@ qg_split split_of(const qgemm_plan* p, int64_t M) {
 }
 
 // The library's own K split (plans of k_parts 1): int4 / uint4 with 33 to 256 rows,
-// N from 4096 and K from 8192, where the tiles that fill the CUs are few and long: two parts
+// N from 4096 and K from 8192, where the tiles that fill the CUs are few and long: as
+// many parts (2, 4 or 8) as one wave of 256 workgroups of 128 x 128 tiles takes,
 // summed in part order (bitwise reproducible).  N = K = 16384, M = 128: 109 -> 91 us
-// (128 x 128 tiles over both parts instead of 64 x 128); N = 4096, K = 11008: 51 ->
-// 40 us.  fp16 and int8 ran slower split (122 / 68 against 120 / 64 us).
+// (two parts of 128 x 128 tiles instead of 64 x 128); N = 4096, K = 11008, M = 128:
+// 51 -> 39 us with two parts, 31 us with eight.  fp16 and int8 ran slower split
+// (122 / 68 against 120 / 64 us).
 #ifndef QG_AUTO_SPLIT
 #define QG_AUTO_SPLIT 1
 #endif
@@ -213,7 +215,10 @@ int auto_parts_of(int fmt, int64_t M, int64_t N, int64_t Kpad, int k_parts, int6
   if (!QG_AUTO_SPLIT || k_parts != 1 || n_units < 2) return 0;
   if (fmt != FMT_I4 && fmt != FMT_U4) return 0;
   if (M <= 32 || M > 256 || Kpad < 8192 || N < 4096) return 0;
-  return 2;
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int kp = 2;
+  while (kp < 8 && tiles * kp * 2 <= 256 && kp * 2 <= n_units) kp *= 2;
+  return kp;
 }
 
 qg_choice choose(const qgemm_plan* p, int64_t M) {
