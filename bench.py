@@ -380,31 +380,40 @@ def targets(out):
 
 def oracle_us(c):
     """Single-thread time of the CPU oracle for one call of a grid entry, extrapolated from
-    a sample: all K, 64 output columns, and all rows up to 64 (else 64): the oracle's
-    cost grows with the columns it unpacks and with rows x columns of its product."""
+    a sample (the best of three runs): all K, 64 output columns, and all rows up to 64
+    (else 64): the oracle's cost grows with the columns it unpacks and with rows x
+    columns of its product."""
     import numpy as np
     import oracle
     import synth
     from threadpoolctl import threadpool_limits
     M, K = c["M"], c["K"]
     Ms = min(M, 64)
+
+    def best_of_3(f):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        return min(ts)
+
     with threadpool_limits(limits=1):
         if c["w"] == "quant":
             A = synth.draw_fp16_activations(Ms, K, seed=1)
-            t0 = time.perf_counter()
-            oracle.quantize_rows(A)
-            return round((time.perf_counter() - t0) * 1e6 * M / Ms, 1)
+            return round(best_of_3(lambda: oracle.quantize_rows(A)) * 1e6 * M / Ms, 1)
         N = c["N"]
         Ns = min(N, 64)
         g = c.get("g", 0) if c["w"] in ("i4", "u4") else 0
         p = synth.make_problem(Ms, Ns, K, c["w"], group_size=g, has_zeros=c.get("zeros", False), seed=1)
-        t0 = time.perf_counter()
         if c.get("dq"):
-            oracle.qgemm_ref_scaled(p.A, p.w, N=Ns, K=K, w_dtype=p.w_dtype,
-                                    row_scales=np.ones(Ms, np.float32), col_scales=np.ones(Ns, np.float32))
+            run = lambda: oracle.qgemm_ref_scaled(p.A, p.w, N=Ns, K=K, w_dtype=p.w_dtype,
+                                                  row_scales=np.ones(Ms, np.float32),
+                                                  col_scales=np.ones(Ns, np.float32))
         else:
-            oracle.qgemm_ref(p.A, p.w, p.s, p.z, N=Ns, K=K, w_dtype=p.w_dtype, group_size=p.group_size)
-        return round((time.perf_counter() - t0) * 1e6 * (N / Ns) * (M / Ms), 1)
+            run = lambda: oracle.qgemm_ref(p.A, p.w, p.s, p.z, N=Ns, K=K, w_dtype=p.w_dtype,
+                                           group_size=p.group_size)
+        return round(best_of_3(run) * 1e6 * (N / Ns) * (M / Ms), 1)
 
 
 def main():
