@@ -35,6 +35,8 @@ BIAS_CASES = [
     (300, 520, 512, "f16", 0, False, 2, "auto"),      # direct-load, ordered partials
     (300, 520, 512, "f16", 0, False, 2, "atomic"),    # direct-load, fp32 atomics + conversion pass
     (160, 264, 1024, "i2", 0, False, 1, "-"),         # direct-load int, stored
+    (40, 264, 1024, "i4", -1, False, 1, "-"),         # direct-load, column scale in the epilogue
+    (300, 520, 1024, "u4", -1, False, 2, "atomic"),   # the same, fp32 atomics + conversion pass
 ]
 
 

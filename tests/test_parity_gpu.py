@@ -247,7 +247,7 @@ DL_SHAPES = [(40, 1000, 1, False), (40, 12000, 1, False), (40, 16376, 2, False),
              (100, 16376, 4, False), (300, 16376, 2, True), (100, 24000, 1, False), (20, 16376, 4, False),
              (400, 16376, 1, False)]
 DL_FORMATS = [("i4", 128, False), ("u4", 128, True), ("u4", 256, False), ("i4", 0, False), ("f16", 0, False),
-              ("i8", 0, False), ("i2", 0, False)]
+              ("i8", 0, False), ("i2", 0, False), ("i4", -1, False)]
 
 
 @pytest.mark.parametrize("M,N,kp,det", DL_SHAPES)

@@ -251,6 +251,7 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
   a.bias = bias;
   a.row_scale = nullptr;
   a.col_scale = nullptr;
+  a.epi_scale = nullptr;
   a.W = static_cast<const uint4*>(packed);
   a.S = p->L.G ? static_cast<const char*>(packed) + p->L.s_offset : nullptr;
   a.C = C;

@@ -663,12 +663,14 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
       if (col >= a.N) continue;
       const float bf = FP && a.out_mode == OUT_STORE ? bias_f(a, col) : 0.f;
       const int bi = !FP && a.out_mode == OUT_STORE ? bias_i(a, col) : 0;
+      const float es = FP && a.epi_scale ? (float)a.epi_scale[col] : 1.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + (wm * WTM + i) * 16 + q * 4 + r;
         if (row >= a.M) continue;
         const size_t o = (size_t)row * a.N + col;
-        const auto v = acc[i][j][r];
+        auto v = acc[i][j][r];
+        if constexpr (FP) v *= es;
         if (a.out_mode == OUT_STORE) {
           if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)(v + bf);
           else if (a.row_scale) static_cast<_Float16*>(a.C)[o] = dq_out(a, row, col, v);
@@ -821,7 +823,16 @@ int choose_dl_tile(int fmt, int64_t M, int64_t N, int k_parts, int smode) {
   return pick;
 }
 
-hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st) {
+hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a0, hipStream_t st) {
+  // One scale group over K and no zero points: the column scale factors out of the
+  // whole sum, so the tiles take the unscaled upcast (exact q rather than q * s rounded
+  // to fp16) and the epilogue scales the fp32 sum; W4A16 g = -1 at 16384^3 then runs
+  // like g = 0
+  RunArgs a = a0;
+  if ((fmt == FMT_I4 || fmt == FMT_U4) && a.smode == SC_BLOCK && a.group_size < 0 && !a.zeros) {
+    a.epi_scale = static_cast<const _Float16*>(a.S);
+    a.smode = SC_NONE;
+  }
   switch (tile) {
     case DL_32x64: return launch_tile<DL_32x64>(fmt, a, st);
     case DL_32x128: return launch_tile<DL_32x128>(fmt, a, st);

@@ -108,6 +108,10 @@ struct RunArgs {
   // (+ bias)); null for int32 output
   const float* row_scale;
   const float* col_scale;
+  // int4 / uint4 with one scale group over K and no zero points on the matrix-core
+  // tiles: the per-column scale applied to the fp32 sum in the epilogue (the tiles
+  // then upcast without it); null otherwise
+  const _Float16* epi_scale;
 };
 
 // bias of output column col (0 without bias): fp16 outputs add it in fp32 before
