@@ -124,12 +124,15 @@ typedef enum {
  *   flags         0, or QGEMM_DETERMINISTIC and / or QGEMM_SPLIT_AUTO.
  *   packed_bytes  out: size of the packed blob for qgemm_pack_weights/qgemm_run.
  *   workspace_bytes out: size of the device workspace qgemm_run needs (0 if none).
- *                 A plan of k_parts 1 may need one too: for I4 / U4 weights with
- *                 33 to 256 rows, N >= 4096 and K >= 8192 the library splits K
- *                 itself (runs of more than 32 rows) into 2, 4 or 8 parts (as many as
- *                 one wave of 256 workgroups of 128 x 128 output tiles takes) and sums
- *                 the partial products in a fixed order, so results stay bitwise
- *                 reproducible; the workspace holds those parts' fp32 partials.
+ *                 A plan of k_parts 1 may need one too: for I4 / U4 weights and
+ *                 K >= 8192 the library splits K itself and sums the partial
+ *                 products in a fixed order, so results stay bitwise reproducible;
+ *                 the workspace holds those parts' fp32 partials.  With 33 to 256
+ *                 rows and N >= 4096: 2, 4 or 8 parts (as many as one wave of 256
+ *                 workgroups of 128 x 128 output tiles takes), for runs of more than
+ *                 32 rows.  With 9 to 32 rows, N <= 4096 and groups of whole
+ *                 superblocks (or none): 4 parts for runs of 17 rows or more when the
+ *                 plan has more than 16 rows, else 2 parts for runs of 9 or more.
  */
 qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K,
                           qgemm_dtype a_dtype, qgemm_dtype w_dtype, qgemm_dtype out_dtype,

@@ -319,9 +319,10 @@ def test_k_granularity_pads_to_whole_blocks(kw, Kpad):
 
 
 def test_library_splits_long_int4_tiles_itself():
-    """k_parts 1 with int4 / uint4, 33..256 rows, N >= 4096, K >= 8192: 2, 4 or 8 parts
-    (enough for 256 workgroups of 128 x 128 tiles) summed in order, so the plan reports a
-    workspace of that many fp32 partials; elsewhere none."""
+    """k_parts 1 with int4 / uint4 and K >= 8192: at 33..256 rows and N >= 4096 2, 4 or 8
+    parts (enough for 256 workgroups of 128 x 128 tiles), at 9..32 rows and N <= 4096 two
+    or four, summed in order, so the plan reports a workspace of that many fp32
+    partials; elsewhere none."""
     for kw, wb_expect in [
         (dict(M=128, N=16384, K=16384), 2 * 128 * 16384 * 4),
         (dict(M=256, N=16384, K=8192), 2 * 256 * 16384 * 4),   # 256 tiles: still two
@@ -329,6 +330,15 @@ def test_library_splits_long_int4_tiles_itself():
         (dict(M=128, N=4096, K=11008), 8 * 128 * 4096 * 4),    # 32 tiles: eight
         (dict(M=40, N=4096, K=8192), 8 * 40 * 4096 * 4),
         (dict(M=256, N=4096, K=11008, group_size=-1, w_dtype="u4", has_zeros=1), 4 * 256 * 4096 * 4),
+        # 9..32 rows at N <= 4096 (the matrix-core GEMV): four parts from 17 rows, two below
+        (dict(M=32, N=4096, K=11008), 4 * 32 * 4096 * 4),
+        (dict(M=20, N=2048, K=8192, group_size=-1), 4 * 20 * 2048 * 4),
+        (dict(M=16, N=4096, K=11008), 2 * 16 * 4096 * 4),
+        (dict(M=9, N=4096, K=8192, w_dtype="u4", has_zeros=1), 2 * 9 * 4096 * 4),
+        (dict(M=8, N=4096, K=11008), 0),                       # GEMV rows
+        (dict(M=32, N=4096, K=4096), 0),                       # short K
+        (dict(M=32, N=8192, K=11008), 0),                      # wide
+        (dict(M=32, N=4096, K=11008, group_size=64), 0),       # per-piece groups
         (dict(M=32, N=16384, K=16384), 0),                     # skinny: matrix-core GEMV
         (dict(M=512, N=16384, K=16384), 0),                    # enough tiles
         (dict(M=128, N=16384, K=4096), 0),                     # short K

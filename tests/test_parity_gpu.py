@@ -356,6 +356,25 @@ def test_k_tail_with_fewer_rows_and_bias(w_dtype, g, zeros, kp):
 
 
 # ---------------------------------------------------------------- the library's own K split
+@pytest.mark.parametrize("M,w_dtype,g,zeros", [(32, "i4", 128, False), (20, "u4", 128, True), (12, "i4", -1, False)])
+def test_library_k_split_skinny(M, w_dtype, g, zeros):
+    """Plans of 9..32 rows at N <= 4096, K >= 8192 (the matrix-core int4 GEMV): the
+    library takes four ordered parts for runs of 17 rows and more (two below 17 rows
+    when the plan itself has at most 16): oracle parity, bitwise repeats, and run-time
+    row counts on both sides of the threshold."""
+    N, K = 4096, 11008
+    say(f"library split skinny M={M} {w_dtype} g={g} zeros={zeros}")
+    c = Case(M, N, K, w_dtype, g, zeros, seed=4500 + M)
+    assert c.q.ws_bytes == (4 if M > 16 else 2) * M * N * 4
+    first = c.run()
+    assert_matches(first, c.reference(), f"skinny split M={M}")
+    assert np.array_equal(c.run(), first)
+    b = synth.draw_bias(N, "f16", 4501)
+    for m in (1, 8, 9, 16, 17, M):
+        if m <= M:
+            assert_matches(c.run(M=m, bias=b), c.reference(rows=np.arange(m), bias=b), f"rows {m} of {M}")
+
+
 @pytest.mark.parametrize("M,w_dtype,g,zeros", [(33, "i4", 128, False), (128, "u4", 128, True),
                                                (256, "i4", -1, False), (100, "u4", 0, False)])
 def test_library_k_split_reproducible(M, w_dtype, g, zeros):

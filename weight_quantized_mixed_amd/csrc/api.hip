@@ -32,7 +32,8 @@ struct qgemm_plan {
   qg_choice ch;      // kernels for M rows (calls with fewer rows choose again)
   int32_t unit_kb, n_units;
   bool two_pass;     // split-K reduced by partials + one ordered pass (else atomics)
-  int32_t auto_parts;  // k_parts 1: parts the library splits K into on its own for M > 32 (0: none)
+  int32_t auto_parts;  // k_parts 1: parts the library splits K into on its own (0: none) ...
+  int32_t auto_min_m;  // ... for runs of at least this many rows
   size_t ws_bytes;
 };
 
@@ -197,28 +198,40 @@ struct qg_split {
   bool two_pass;
 };
 qg_split split_of(const qgemm_plan* p, int64_t M) {
-  if (p->auto_parts > 1 && M > 32) return {p->auto_parts, true};
+  if (p->auto_parts > 1 && M >= p->auto_min_m) return {p->auto_parts, true};
   return {p->k_parts, p->two_pass};
 }
 
-// The library's own K split (plans of k_parts 1): int4 / uint4 with 33 to 256 rows,
-// N from 4096 and K from 8192, where the tiles that fill the CUs are few and long: as
-// many parts (2, 4 or 8) as one wave of 256 workgroups of 128 x 128 tiles takes,
-// summed in part order (bitwise reproducible).  N = K = 16384, M = 128: 109 -> 91 us
+// The library's own K split (plans of k_parts 1), summed in part order (bitwise
+// reproducible).  int4 / uint4 with 33 to 256 rows, N from 4096 and K from 8192, where
+// the tiles that fill the CUs are few and long: as many parts (2, 4 or 8) as one wave
+// of 256 workgroups of 128 x 128 tiles takes.  N = K = 16384, M = 128: 109 -> 91 us
 // (two parts of 128 x 128 tiles instead of 64 x 128); N = 4096, K = 11008, M = 128:
 // 51 -> 39 us with two parts, 31 us with eight.  fp16 and int8 ran slower split
 // (122 / 68 against 120 / 64 us).
 #ifndef QG_AUTO_SPLIT
 #define QG_AUTO_SPLIT 1
 #endif
-int auto_parts_of(int fmt, int64_t M, int64_t N, int64_t Kpad, int k_parts, int64_t n_units) {
-  if (!QG_AUTO_SPLIT || k_parts != 1 || n_units < 2) return 0;
-  if (fmt != FMT_I4 && fmt != FMT_U4) return 0;
-  if (M <= 32 || M > 256 || Kpad < 8192 || N < 4096) return 0;
+// And the matrix-core int4 GEMV at 9 to 32 rows with N up to 4096 and K from 8192,
+// whose 16-column workgroups would otherwise each read all of A: four parts from 17
+// rows, two from 9, so 64-column workgroups fill the CUs (M = 32, N = 4096, K = 11008:
+// 22.5 -> 15.3 us; M = 16: 13.3 -> 11.7 us; one part stayed fastest at the other
+// LLaMA shapes and at N = K = 16384).
+struct qg_auto {
+  int parts, min_m;
+};
+qg_auto auto_parts_of(int fmt, int32_t group_size, int64_t M, int64_t N, int64_t Kpad, int k_parts,
+                      int64_t n_units) {
+  if (!QG_AUTO_SPLIT || k_parts != 1 || n_units < 2) return {0, 0};
+  if (fmt != FMT_I4 && fmt != FMT_U4) return {0, 0};
+  if (Kpad < 8192) return {0, 0};
+  if (M > 8 && M <= 32 && N <= 4096 && scale_mode(fmt, group_size) != SC_PIECE && n_units >= 4)
+    return M > 16 ? qg_auto{4, 17} : qg_auto{2, 9};
+  if (M <= 32 || M > 256 || N < 4096) return {0, 0};
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int kp = 2;
   while (kp < 8 && tiles * kp * 2 <= 256 && kp * 2 <= n_units) kp *= 2;
-  return kp;
+  return {kp, 33};
 }
 
 qg_choice choose(const qgemm_plan* p, int64_t M) {
@@ -453,7 +466,9 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   fill_layout(&p->L, fmt, N, K, group_size, has_zeros != 0);
   p->unit_kb = (int32_t)(unit / KB);
   p->n_units = (int32_t)n_units;
-  p->auto_parts = auto_parts_of(fmt, M, N, Kpad, k_parts, n_units);
+  const qg_auto au = auto_parts_of(fmt, group_size, M, N, Kpad, k_parts, n_units);
+  p->auto_parts = au.parts;
+  p->auto_min_m = au.min_m;
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   p->two_pass = k_parts > 1 && two_pass_split(M, mn4 * (size_t)k_parts, out_dtype == QGEMM_F16, flags);
   p->ch = choose(p, M);
