@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqgemm.so")
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv16.hip", "mfma.hip", "mfma_dl.hip", "reduce.hip", "quant.hip", "gemv_mfma.hip", "gemv_mfma4.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv16.hip", "mfma.hip", "mfma_dl.hip", "mfma_big.hip", "reduce.hip", "quant.hip", "gemv_mfma.hip", "gemv_mfma4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 vector ops are disabled for every device pass

@@ -164,6 +164,10 @@ enum DlTile : int {
 void dl_tile_dims(int tile, int* bm, int* bn);
 int choose_dl_tile(int fmt, int64_t M, int64_t N, int k_parts, int smode);
 hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st);
+// 256 x 256 tiles of four 128 x 128 waves (mfma_big.hip) for the formats that
+// big_tile_takes; same arguments and stage layout as launch_mfma_dl's 256 x 256 tile
+bool big_tile_takes(int fmt, const RunArgs& a);
+hipError_t launch_mfma_big(int fmt, const RunArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // dst[m, k] = k < K ? A[m, k] : 0 for rows of Kpad elements of esz bytes (Kpad * esz a
 // multiple of 16, dst 16-byte aligned; A any alignment of its element size)
