@@ -262,6 +262,27 @@ def test_direct_load_tiles(M, N, kp, det, w_dtype, g, zeros):
     assert_matches(gpu[:, cols], c.reference(cols=cols), f"dl {w_dtype} M={M} kp={kp}")
 
 
+# ---------------------------------------------------------------- four-group tiles, odd superblock counts
+# The int4 tiles of four K groups (32x64 at 40 and 100 rows of 1000 columns, 32x128 at
+# 40 rows of 12000) load four stages, two superblocks, per round; a part of an odd
+# number of superblocks ends inside a round, whose missing stages are clamped copies,
+# and scale groups of two or three superblocks change inside a round.
+ODD_SB_SHAPES = [(40, 1000, 1), (40, 1000, 3), (100, 1000, 3), (40, 12000, 2)]
+ODD_SB_FORMATS = [("i4", 128, False, 4224), ("u4", 128, True, 4224), ("i4", 0, False, 4224),
+                  ("u4", 256, False, 4352), ("i4", 384, False, 4224)]
+
+
+@pytest.mark.parametrize("M,N,kp", ODD_SB_SHAPES)
+@pytest.mark.parametrize("w_dtype,g,zeros,K", ODD_SB_FORMATS)
+def test_direct_load_odd_superblocks(M, N, kp, w_dtype, g, zeros, K):
+    say(f"odd superblocks M={M} N={N} K={K} {w_dtype} g={g} zeros={zeros} kp={kp}")
+    c = Case(M, N, K, w_dtype, g, zeros, k_parts=kp, seed=5 * M + kp + g)
+    rng = np.random.default_rng(M + N + kp)
+    cols = np.unique(np.concatenate([rng.choice(N, min(N, 300), replace=False), [0, 63, 64, N - 1]]))
+    gpu = c.run()
+    assert_matches(gpu[:, cols], c.reference(cols=cols), f"odd superblocks {w_dtype} g={g} M={M} kp={kp}")
+
+
 # ---------------------------------------------------------------- HIP graph capture
 GRAPH_CASES = [(1, 200, 1024, "i4", 128, False, 1, False), (1, 2752, 1024, "i2", 0, False, 3, False),
                (4, 300, 1024, "u4", 128, True, 1, False), (40, 264, 1024, "i4", 128, False, 2, False),

@@ -62,6 +62,12 @@ using namespace dl;
 #ifndef QG_DL_IL
 #define QG_DL_IL 1
 #endif
+// int4 / uint4 tiles of four K groups: issue whole rounds from per-round bases (1) or
+// stage by stage (0).  Measured at M = 128, N = K = 4096 (32 x 64 tiles): 22.1 -> 17.5 us;
+// the two-group tiles and int2 stayed level or lost 1-3 % with it and keep stages.
+#ifndef QG_DL_ROUNDS
+#define QG_DL_ROUNDS 1
+#endif
 // int4 / int2 stages: 0 keeps the upcasts in a run after each step's MFMAs,
 // 1 spreads them word by word, 2 column block by column block (per tile height)
 #ifndef QG_DL_IL_P
@@ -290,6 +296,85 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
     static_for(std::make_integer_sequence<int, NDMA>{}, [&](auto E) { dma_one(sa, E); });
   };
 
+  // Round issue (four K groups, int4 / uint4 weights).  A superblock is two stages and
+  // every part starts on one, so the KS stages of round r (part stages r KS ..
+  // r KS + KS - 1) are KS / 2 whole superblocks: stage k reads the round's
+  // activation columns + 128 k bytes, half k % 2 of weight superblock row k / 2, and
+  // the scales of its group, at most one group boundary into the round (groups are
+  // whole superblocks, rounds at most two).  Only waves that own direct loads keep
+  // these bases, advanced once per round instead of stage by stage.  A round past
+  // the part's last stage issues nothing (the waits then drain all loads); one that
+  // ends past it takes the per-stage path above with its clamped copies.
+  constexpr bool ROUNDS = QG_DL_ROUNDS && KS == 4 && I4 && BSB == 512 && ROWB == 128;
+  constexpr int NR = NSTAGE / KS;  // rounds in the ring
+  struct RoundSrc {
+    const uint8_t* a;   // activations of the round's first stage
+    const uint8_t* w;   // weight superblock row of stages 0, 1
+    const uint8_t* w2;  // of stages 2, 3 (KS = 4)
+    const uint8_t* s;   // scales of the first stage's group
+    int pig;            // position of the first stage in its group
+    uint32_t dst;       // ring slot of the first stage
+  } rs{};
+  const int grp_pos = SCALED && a.group_size > 0 ? a.group_size : (1 << 30);  // positions per group
+  const size_t srow = (size_t)a.Npad * bytes_per_scale;
+  const size_t sbrow = (size_t)a.NB * 1024;  // one superblock row of the blob
+  if constexpr (ROUNDS) {
+    rs.dst = next.dst;
+    rs.a = next.a;
+    rs.w = next.w;
+    rs.w2 = next.w + sbrow;
+    rs.s = next.s;
+    rs.pig = SCALED && a.group_size > 0 ? (int)(((int64_t)s0 * SPOS) % a.group_size) : 0;
+  }
+  auto issue_round = [&](int ri) {
+    if (ri * KS >= nst) return;  // past the part: nothing
+    if (ri * KS + KS > nst) {
+      // the part ends inside this round: stage by stage with clamped sources
+      next.dst = rs.dst;
+      next.a = rs.a;
+      next.w = rs.w;
+      next.s = rs.s;
+      grp_left = (grp_pos - rs.pig) / SPOS;
+      next_st = ri * KS;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) issue();
+      return;
+    }
+    static_for(std::make_integer_sequence<int, KS>{}, [&](auto K) {
+      constexpr int k = decltype(K)::value;
+      const uint32_t dst = rs.dst + k * STAGE;
+      static_for(std::make_integer_sequence<int, NDMA>{}, [&](auto E) {
+        constexpr int e = decltype(E)::value;
+        if constexpr (e < A_MAX) {
+          if (NS_A % NWT == 0 || e < la) dma16s(rs.a, a_off[e] + k * 128, dst + (e * NWT + wave) * 1024);
+        } else if constexpr (e < A_MAX + B_MAX) {
+          constexpr int i = e - A_MAX;
+          if (NS_B % NWT == 0 || i < lb)
+            dma16s(k < 2 ? rs.w : rs.w2, b_off[i] + (k % 2) * 512, dst + A_BYTES + (i * NWT + wave) * 1024);
+        } else if (wave == 0) {
+          const uint8_t* sp = rs.pig + k * SPOS >= grp_pos ? rs.s + srow : rs.s;
+          dma16s(sp, s_off, dst + A_BYTES + B_BYTES);
+        }
+      });
+    });
+    // advance the bases by one round
+    rs.dst = rs.dst + KS * STAGE == lds_end ? lds0 : rs.dst + KS * STAGE;
+    rs.a += KS * 128;
+    rs.w += (KS / 2) * sbrow;
+    if constexpr (KS == 4) rs.w2 += 2 * sbrow;
+    if constexpr (SCALED) {
+      rs.pig += KS * SPOS;
+      if (rs.pig >= grp_pos) {
+        rs.pig -= grp_pos;
+        rs.s += srow;
+      }
+      if (rs.pig >= grp_pos) {
+        rs.pig -= grp_pos;
+        rs.s += srow;
+      }
+    }
+  };
+
   acc_v acc[WTM][WTN];
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
@@ -490,9 +575,18 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   };
 
   // prologue: NSTAGE stages in flight, then the fragments of step 0
+  if constexpr (ROUNDS) {
+    if (my_loads > 0) {
 #pragma unroll
-  for (int st = 0; st < NSTAGE; ++st) issue();
-  wait_loads<G::LMIN, G::LMAX, NSTAGE - KS>(my_loads);
+      for (int r = 0; r < NR; ++r) issue_round(r);
+    }
+    if ((NR - 1) * KS < nst) wait_loads<G::LMIN, G::LMAX, NSTAGE - KS>(my_loads);
+    else wait_vm_lgkm0<0>();  // some rounds of the ring were not issued
+  } else {
+#pragma unroll
+    for (int st = 0; st < NSTAGE; ++st) issue();
+    wait_loads<G::LMIN, G::LMAX, NSTAGE - KS>(my_loads);
+  }
   asm volatile("s_barrier" ::: "memory");
 
   Frag X, Y;
@@ -544,7 +638,16 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
       fence();
       read_step(Y, s, std::integral_constant<int, 1>{});
       if (live) compute(X, Y);
-      sync_round(r + 1);  // past the last round this reads clamped copies that are never used
+      if constexpr (ROUNDS) {
+        // round r + 1 landed: rounds r + 2 .. r + NR - 1 may still be in flight, when
+        // they were issued; then round r + NR into the slots of round r
+        if ((r + NR - 1) * KS < nst) wait_loads<G::LMIN, G::LMAX, NSTAGE - 2 * KS>(my_loads);
+        else wait_vm_lgkm0<0>();
+        asm volatile("s_barrier" ::: "memory");
+        if (my_loads > 0) issue_round(r + NR);
+      } else {
+        sync_round(r + 1);  // past the last round this reads clamped copies that are never used
+      }
       fence();
       read_step(X, s + KS, std::integral_constant<int, 0>{});
       if (live) compute(Y, X);
