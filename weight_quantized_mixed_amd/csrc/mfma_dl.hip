@@ -68,6 +68,9 @@ using namespace dl;
 #ifndef QG_DL_ROUNDS
 #define QG_DL_ROUNDS 1
 #endif
+#ifndef QG_DL_KG_ORDER
+#define QG_DL_KG_ORDER 1
+#endif
 // int4 / int2 stages: 0 keeps the upcasts in a run after each step's MFMAs,
 // 1 spreads them word by word, 2 column block by column block (per tile height)
 #ifndef QG_DL_IL_P
@@ -442,10 +445,13 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
       }
     }
   };
+  // (the weight words first: the upcasts that wait for them then leave the
+  // activation reads in flight)
   auto read_step = [&](Frag& f, int s, auto T) {
     const uint8_t* base = slot(s);
-    static_for(std::make_integer_sequence<int, WTM>{}, [&](auto I) { read_a(f, base, T, I); });
     static_for(std::make_integer_sequence<int, WTN>{}, [&](auto J) { read_b(f, base, T, J); });
+    if constexpr (QG_DL_KG_ORDER) fence();
+    static_for(std::make_integer_sequence<int, WTM>{}, [&](auto I) { read_a(f, base, T, I); });
   };
 
   // upcast of word jj of column block j's MFMA operand from its packed word
@@ -494,12 +500,20 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
   };
 
   // one MFMA step on cur while nxt (already read) is upcast, block by block
+  // (each column block's MFMAs issue before the upcast that may wait for its reads)
   auto compute = [&](const Frag& cur, Frag& nxt) {
     fence();
-    static_for(std::make_integer_sequence<int, WTN>{}, [&](auto J) {
-      mma(cur, decltype(J)::value);
-      make_b(nxt, J);
-    });
+    if constexpr (QG_DL_KG_ORDER) {
+      static_for(std::make_integer_sequence<int, WTN>{}, [&](auto J) { mma(cur, decltype(J)::value); });
+      fence();
+      static_for(std::make_integer_sequence<int, WTN>{}, [&](auto J) { make_b(nxt, J); });
+    } else {
+      static_for(std::make_integer_sequence<int, WTN>{}, [&](auto J) {
+        mma(cur, decltype(J)::value);
+        fence();
+        make_b(nxt, J);
+      });
+    }
     fence();
   };
 
