@@ -329,7 +329,11 @@ def test_library_splits_long_int4_tiles_itself():
         (dict(M=128, N=8192, K=8192), 4 * 128 * 8192 * 4),     # 64 tiles: four
         (dict(M=128, N=4096, K=11008), 8 * 128 * 4096 * 4),    # 32 tiles: eight
         (dict(M=40, N=4096, K=8192), 8 * 40 * 4096 * 4),
-        (dict(M=256, N=4096, K=11008, group_size=-1, w_dtype="u4", has_zeros=1), 4 * 256 * 4096 * 4),
+        # uint4 with zero points from 129 rows: also the row sums and the -s z columns
+        # that runs of fewer rows on the 256 x 256 tiles would need (two bf16 planes of
+        # one group padded to 32 for each row and each of the 4096 columns)
+        (dict(M=256, N=4096, K=11008, group_size=-1, w_dtype="u4", has_zeros=1),
+         4 * 256 * 4096 * 4 + (256 + 4096) * 32 * 2 * 2),
         # 9..32 rows at N <= 4096 (the matrix-core GEMV): four parts from 17 rows, two below
         (dict(M=32, N=4096, K=11008), 4 * 32 * 4096 * 4),
         (dict(M=20, N=2048, K=8192, group_size=-1), 4 * 20 * 2048 * 4),

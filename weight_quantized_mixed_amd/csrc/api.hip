@@ -292,6 +292,10 @@ RunArgs make_args(const qgemm_plan* p, const qg_choice& ch, int64_t M, const voi
   a.gemv_cb = ch.gemv_cb;
   a.sb_per_group = p->group_size > KB ? p->group_size / KB : p->group_size < 0 ? (int32_t)p->L.nkb : 1;
   a.out_mode = sp.kp == 1 ? OUT_STORE : sp.two_pass ? OUT_PARTIAL : OUT_ATOMIC;
+  a.zr = nullptr;
+  a.zp = nullptr;
+  a.zr_gp = 0;
+  a.zr_G = 0;
   return a;
 }
 
@@ -311,10 +315,38 @@ size_t split_ws_bytes(const qgemm_plan* p, int64_t M) {
 }
 size_t a_esz(const qgemm_plan* p) { return p->a_dtype == QGEMM_F16 ? 2 : 1; }
 size_t pad_offset(const qgemm_plan* p, int64_t M) { return (size_t)round_up((int64_t)split_ws_bytes(p, M), 256); }
-size_t run_ws_bytes(const qgemm_plan* p, int64_t M) {
+size_t split_pad_bytes(const qgemm_plan* p, int64_t M) {
   if (p->L.Kpad == p->K) return split_ws_bytes(p, M);
   return pad_offset(p, M) + (size_t)M * (size_t)p->L.Kpad * a_esz(p);
 }
+
+// Zero-point folding: uint4 with zero points and groups of whole superblocks (or one
+// over K) runs on the four-wave 256 x 256 tiles with the zero points taken out of the
+// K loop, C = sum_k A q s - sum_g R[m, g] s z, after two passes that write the row sums
+// of A over the groups (R) and P = -s z, each as two bf16 planes of round_up(G, 32)
+// values per row or column, at the end of the workspace.  The eight-wave tile with
+// the zero points in its loop measured 7.6-7.8 ms at M = N = K = 16384.
+#ifndef QG_ZERO_FOLD
+#define QG_ZERO_FOLD 1
+#endif
+bool zero_fold_format(const qgemm_plan* p) {
+  return QG_ZERO_FOLD && QG_BIG4 && p->L.fmt == FMT_U4 && p->L.zeros &&
+         scale_mode(p->L.fmt, p->group_size) == SC_BLOCK && p->L.Kpad / 32 <= ROWSUM_MAX_UNITS;
+}
+bool zero_fold(const qgemm_plan* p, const qg_choice& ch) {
+  return zero_fold_format(p) && ch.path == QGEMM_PATH_MFMA && ch.dl_tile == DL_256x256;
+}
+int64_t zr_gp_of(const qgemm_plan* p) { return round_up(p->L.G, 32); }
+size_t zr_offset(const qgemm_plan* p, int64_t M) { return (size_t)round_up((int64_t)split_pad_bytes(p, M), 256); }
+size_t zp_offset(const qgemm_plan* p, int64_t M) {
+  return zr_offset(p, M) + (size_t)round_up(M * zr_gp_of(p) * 2 * (int64_t)sizeof(uint16_t), 256);
+}
+size_t run_ws_bytes_for(const qgemm_plan* p, int64_t M, bool fold) {
+  if (!fold) return split_pad_bytes(p, M);
+  return zp_offset(p, M) + (size_t)p->L.Npad * (size_t)zr_gp_of(p) * 2 * sizeof(uint16_t);
+}
+// the workspace of a run of M rows with the kernels chosen for M
+size_t run_ws_bytes(const qgemm_plan* p, int64_t M, const qg_choice& ch) { return run_ws_bytes_for(p, M, zero_fold(p, ch)); }
 
 // one run: the split-K fill, the kernel chosen for M rows, the finalize pass
 qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const void* packed, const void* bias,
@@ -322,7 +354,9 @@ qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const vo
                       size_t workspace_bytes, void* stream) {
   if (!plan || !A || !packed || !C) return QGEMM_ERR_INVALID_ARG;
   if (M < 1 || M > plan->M) return QGEMM_ERR_INVALID_ARG;
-  const size_t need = run_ws_bytes(plan, M);
+  const qg_choice ch = M == plan->M ? plan->ch : choose(plan, M);
+  const bool fold = zero_fold(plan, ch);
+  const size_t need = run_ws_bytes(plan, M, ch);
   if (need && (!workspace || workspace_bytes < need)) return QGEMM_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(packed) |
        reinterpret_cast<uintptr_t>(workspace)) & 15)
@@ -333,7 +367,6 @@ qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const vo
   if ((reinterpret_cast<uintptr_t>(row_scales) | reinterpret_cast<uintptr_t>(col_scales)) & 3)
     return QGEMM_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const qg_choice ch = M == plan->M ? plan->ch : choose(plan, M);
   RunArgs a = make_args(plan, ch, M, A, packed, bias, C, workspace);
   a.row_scale = row_scales;
   a.col_scale = col_scales;
@@ -346,6 +379,16 @@ qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const vo
     e = launch_pad_rows(A, Ap, M, plan->K, plan->L.Kpad, (int)a_esz(plan), st);
     a.A = Ap;
     a.K = (int32_t)plan->L.Kpad;
+  }
+  if (e == hipSuccess && fold) {
+    uint16_t* zr = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + zr_offset(plan, M));
+    uint16_t* zp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + zp_offset(plan, M));
+    a.zr_gp = (int32_t)zr_gp_of(plan);
+    a.zr_G = (int32_t)plan->L.G;
+    e = launch_group_rowsum(a, zr, st);
+    if (e == hipSuccess) e = launch_zero_planes(a, zp, st);
+    a.zr = zr;
+    a.zp = zp;
   }
   if (e == hipSuccess && a.out_mode == OUT_ATOMIC)
     e = out_f16 ? launch_fill_zero(workspace, (size_t)M * plan->N * 4, st)  // fp32 / int32 accumulator
@@ -472,7 +515,10 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   p->two_pass = k_parts > 1 && two_pass_split(M, mn4 * (size_t)k_parts, out_dtype == QGEMM_F16, flags);
   p->ch = choose(p, M);
-  p->ws_bytes = run_ws_bytes(p, M);  // int32 output with atomics: none (straight into C)
+  // int32 output with atomics: none (straight into C).  With zero-point folding the
+  // row sums are counted whenever M could take the 256 x 256 tiles, so that runs of
+  // fewer rows never need more than the plan states
+  p->ws_bytes = run_ws_bytes_for(p, M, zero_fold_format(p) && (zero_fold(p, p->ch) || M > 128));
   if (packed_bytes) *packed_bytes = p->L.total;
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
   *out = p;
@@ -500,7 +546,7 @@ qgemm_status qgemm_run_noalloc(const qgemm_plan* plan, int64_t M, const void* A,
                                const void* bias, void* C, void* stream) {
   if (!plan || dequant_plan(plan)) return QGEMM_ERR_INVALID_ARG;
   if (M < 1 || M > plan->M) return QGEMM_ERR_INVALID_ARG;
-  const size_t need = run_ws_bytes(plan, M);
+  const size_t need = run_ws_bytes(plan, M, M == plan->M ? plan->ch : choose(plan, M));
   if (need > QGEMM_NOALLOC_MAX_SCRATCH) return QGEMM_ERR_UNSUPPORTED;
   void* ws = nullptr;
   if (need) {

@@ -1,5 +1,5 @@
-// Large-tile matrix-core path for fp16 weights and for int4 / uint4 weights without
-// zero points: 256 x 256 output tiles computed by four waves, each owning a 128 x 128
+// Large-tile matrix-core path for fp16 and int4 / uint4 weights: 256 x 256 output
+// tiles computed by four waves, each owning a 128 x 128
 // quadrant (64 MFMA tiles of 16 x 16, whose accumulators live in the accumulation
 // registers), from a ring of 2 to 4 LDS stages that global_load_lds_dwordx4 fills
 // straight from memory.  This is the shape of the large-M products in the BitBLAS
@@ -25,6 +25,13 @@
 // step (issued as a burst after the barrier they filled the texture path's queue and
 // held the matrix cores 47 % idle), the fragment reads after every other MFMA of the
 // first half, the upcasts from the 16th MFMA on.
+//
+// Scaled uint4 is upcast and scaled by one packed fp16 fma per pair, (1024 + q) s +
+// c; with zero points the fma's addend holds the zero point rounded to an integer,
+// and what it leaves (the fraction of z and the rounding of the addend, a constant
+// per column and group) is added after the loop as sum_g R[m, g] P[g, n] by bf16
+// MFMAs over the groups (R the row sums of A over each group, both R and P written
+// by passes before the kernel), so the loop costs what unscaled int4 costs.
 //
 // Tiles are numbered as in mfma_dl.hip: each XCD owns a contiguous band of tiles,
 // swept in column-major groups of tile rows.
@@ -79,6 +86,9 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
   using G = BigGeo<FMT, SCALED>;
   constexpr bool FP = G::FP, PACKED = G::PACKED;
   constexpr bool I4 = FMT == FMT_I4 || FMT == FMT_U4;
+  // scaled uint4: the upcast and scale fold into one packed fma (needs -1024 s, or with
+  // zero points -fp16(1024 + z) s, finite in fp16: |s| < 64, |s (1024 + z)| < 65504)
+  constexpr bool U4S = FMT == FMT_U4 && SCALED;
   constexpr int KB = G::KB, ESZ = G::ESZ, ROWB = G::ROWB, SPOS = G::SPOS, BSB = G::BSB;
   constexpr int A_BYTES = G::A_BYTES, B_BYTES = G::B_BYTES, STAGE = G::STAGE, NSTAGE = G::NSTAGE;
   constexpr int LA = G::LA, LB = G::LB, L = G::L;
@@ -204,7 +214,8 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
     uint32_t k_exp;
     asm("v_mov_b32 %0, 0x64006400" : "=v"(k_exp));
     uint32_t rw[8];          // int4 / int2: packed word of column block j
-    uint32_t sc[8], zc[8];   // scale (and zero) of column block j, both halves
+    uint32_t sc[8];          // scale of column block j, both halves
+    uint32_t nc[8];          // uint4: the fma's addend, -1024 s (with zero points -fp16(1024 + z) s)
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
     auto read_a = [&](Frag& f, const uint8_t* base, auto T, auto I) {
@@ -224,14 +235,20 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
         f.b[j] = *reinterpret_cast<const uint4*>(lb + t * 1024 + lane * 16);  // superblock t, piece = lane
       if constexpr (SCALED && t == 0) {
         const int col = (wn * 8 + j) * 16 + l16;
+        // with zero points the slot holds (scale, zero) pairs; the zero points are
+        // applied after the loop
+        const uint32_t u = ZEROS ? *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4)
+                                 : *reinterpret_cast<const uint16_t*>(base + A_BYTES + B_BYTES + col * 2);
+        sc[j] = __builtin_amdgcn_perm(u, u, 0x01000100u);  // low half in both halves
         if constexpr (ZEROS) {
-          const uint32_t u = *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4);
-          sc[j] = __builtin_amdgcn_perm(u, u, 0x01000100u);  // low half in both halves
-          zc[j] = __builtin_amdgcn_perm(u, u, 0x03020302u);  // high half in both halves
-        } else {
-          const uint32_t u = *reinterpret_cast<const uint16_t*>(base + A_BYTES + B_BYTES + col * 2);
-          sc[j] = __builtin_amdgcn_perm(u, u, 0x01000100u);
-          zc[j] = 0;
+          // b = fp16(1024 + z) = 1024 + r with r = rne(z) for 0 <= z < 1024 (the fp16
+          // spacing there is 1), and c = fp16(-b s): the fma below then gives
+          // (q - r) s + d rounded once, with d = c + b s the rounding of c, and
+          // -(z - r) s - d goes with the zero points after the loop
+          const uint32_t b = as_u32(as_h2(__builtin_amdgcn_perm(u, u, 0x03020302u)) + as_h2(k_exp));
+          nc[j] = as_u32(as_h2(b) * -as_h2(sc[j]));
+        } else if constexpr (U4S) {
+          nc[j] = as_u32(as_h2(sc[j]) * as_h2(0xE400E400u));  // -1024 s, exact
         }
       }
     };
@@ -242,10 +259,17 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
         const uint32_t wd = rw[j];
         uint32_t o;
         if constexpr (I4) {
-          constexpr uint32_t bias = (FMT == FMT_I4) ? 0x64086408u : 0x64006400u;
-          half2v v = as_h2(((wd >> (4 * jj)) & k_nib) | k_exp) - as_h2(bias);
-          if constexpr (ZEROS) v = v - as_h2(zc[j]);
-          if constexpr (SCALED) v = v * as_h2(sc[j]);
+          const half2v x = as_h2(((wd >> (4 * jj)) & k_nib) | k_exp);  // 1024 + the stored nibble
+          half2v v;
+          if constexpr (U4S) {
+            // (1024 + q) s - 1024 s with one rounding: q s rounded to nearest, as the
+            // subtraction and product would give it, in one instruction (with zero
+            // points (q - r) s + d, see nc)
+            v = __builtin_elementwise_fma(x, as_h2(sc[j]), as_h2(nc[j]));
+          } else {
+            v = x - as_h2((FMT == FMT_I4) ? 0x64086408u : 0x64006400u);
+            if constexpr (SCALED) v = v * as_h2(sc[j]);
+          }
           o = as_u32(v);
         } else if constexpr (jj < 3) {
           o = __builtin_amdgcn_perm(0u, 0x0100FFFEu, (wd >> (2 * jj)) & 0x03030303u);  // 0..3 -> -2..1
@@ -342,6 +366,48 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
     }
     wait_vmcnt<0>();  // drain the tail copies before the workgroup's LDS is released
   }
+  if constexpr (ZEROS) {
+    // The zero points, applied after the loop: acc += sum over groups g of R[m, g]
+    // P[g, n] with P = -(z - r) s - d (the part of the zero point and the rounding of
+    // the fma's addend that the loop left, see nc; R: the rows of A summed over each
+    // group), on the matrix
+    // cores with split bf16 operands, R_hi P_hi + R_hi P_lo + R_lo P_hi (about 16
+    // significant bits, and the fp32 range), both read from the planes a pass over A
+    // and the scale table wrote before this kernel.  The groups are the K of these
+    // products: lane group q of step kk takes groups 32 kk + 8 q .. + 7 in both
+    // operands.  Only part 0 adds it.
+    if (part == 0) {
+      const int gp = a.zr_gp;
+      auto mma_bf16 = [&acc](const uint4& x, const uint4& y, auto K) {
+        constexpr int k = decltype(K)::value, i = k % 8, j = k / 8;
+        // wait states first, in case the compiler copied an operand just before
+        asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                     : "+a"(acc[i][j])
+                     : "v"(__builtin_bit_cast(int4v, x)), "v"(__builtin_bit_cast(int4v, y)));
+      };
+      for (int kk = 0; kk < gp / 32; ++kk) {
+        const int g0 = kk * 32 + q * 8;
+        uint4 rh[8], rl[8], ph[8], pl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = min(m0 + wm * 128 + i * 16 + l16, a.M - 1);
+          const uint16_t* r = a.zr + (size_t)row * 2 * gp + g0;
+          rh[i] = *reinterpret_cast<const uint4*>(r);
+          rl[i] = *reinterpret_cast<const uint4*>(r + gp);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = n0 + wn * 128 + j * 16 + l16;  // < Npad
+          const uint16_t* pz = a.zp + (size_t)col * 2 * gp + g0;
+          ph[j] = *reinterpret_cast<const uint4*>(pz);
+          pl[j] = *reinterpret_cast<const uint4*>(pz + gp);
+        }
+        static_for(std::make_integer_sequence<int, 64>{}, [&](auto K) { mma_bf16(rh[K % 8], ph[K / 8], K); });
+        static_for(std::make_integer_sequence<int, 64>{}, [&](auto K) { mma_bf16(rh[K % 8], pl[K / 8], K); });
+        static_for(std::make_integer_sequence<int, 64>{}, [&](auto K) { mma_bf16(rl[K % 8], ph[K / 8], K); });
+      }
+    }
+  }
   // the last MFMAs' results are read below: more wait states than any MFMA's passes
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
@@ -391,7 +457,9 @@ hipError_t launch_big_t(const RunArgs& a, hipStream_t st) {
 }  // namespace
 
 bool big_tile_takes(int fmt, const RunArgs& a) {
-  return fmt == FMT_F16 || ((fmt == FMT_I4 || fmt == FMT_U4) && !a.zeros);
+  // uint4 with zero points only with the group row sums that fold them out of the loop
+  return fmt == FMT_F16 || ((fmt == FMT_I4 || fmt == FMT_U4) && !a.zeros) ||
+         (fmt == FMT_U4 && a.zeros && a.zr && a.smode == SC_BLOCK);
 }
 
 hipError_t launch_mfma_big(int fmt, const RunArgs& a, hipStream_t st) {
@@ -400,7 +468,7 @@ hipError_t launch_mfma_big(int fmt, const RunArgs& a, hipStream_t st) {
     case FMT_F16: return launch_big_t<FMT_F16, false, false>(a, st);
     case FMT_I4: return sc ? launch_big_t<FMT_I4, true, false>(a, st) : launch_big_t<FMT_I4, false, false>(a, st);
     case FMT_U4:
-      if (a.zeros) return hipErrorInvalidValue;
+      if (a.zeros) return a.zr && sc ? launch_big_t<FMT_U4, true, true>(a, st) : hipErrorInvalidValue;
       return sc ? launch_big_t<FMT_U4, true, false>(a, st) : launch_big_t<FMT_U4, false, false>(a, st);
   }
   return hipErrorInvalidValue;

@@ -39,9 +39,6 @@ namespace qg {
 namespace {
 using namespace dl;
 
-#ifndef QG_BIG4
-#define QG_BIG4 1
-#endif
 #ifndef QG_DL_GROUP_M
 #define QG_DL_GROUP_M 8
 #endif

@@ -112,6 +112,16 @@ struct RunArgs {
   // tiles: the per-column scale applied to the fp32 sum in the epilogue (the tiles
   // then upcast without it); null otherwise
   const _Float16* epi_scale;
+  // uint4 with zero points on the 256 x 256 tiles of four waves: the zero points are
+  // folded out of the K loop (C = sum_k A q s - sum_g R[m, g] s[g, n] z[g, n], R the
+  // row sums of A over scale group g).  zr holds R of each row, zp P = -s z of each
+  // column (Npad of them), each as two bf16 planes of zr_gp values, [hi | lo] with
+  // hi = bf16(x), lo = bf16(x - hi), groups zr_G .. zr_gp - 1 zero; both null when the
+  // zero points stay in the loop
+  const uint16_t* zr;
+  const uint16_t* zp;
+  int32_t zr_gp;  // groups per plane: zr_G rounded up to 32
+  int32_t zr_G;   // scale groups over K
 };
 
 // bias of output column col (0 without bias): fp16 outputs add it in fp32 before
@@ -145,6 +155,12 @@ __device__ __forceinline__ void part_units(const RunArgs& a, int part, int& u0, 
   }
 }
 
+// the 256 x 256 tiles of four 128 x 128 waves (mfma_big.hip) for the formats that
+// take them (0: the eight-wave tile of mfma_dl.hip for every format)
+#ifndef QG_BIG4
+#define QG_BIG4 1
+#endif
+
 // kernel launchers (return hipSuccess or the launch error)
 hipError_t launch_pack(const Layout& L, const void* w, const void* s, const void* z, void* packed,
                        hipStream_t st);
@@ -169,6 +185,14 @@ hipError_t launch_mfma_dl(int fmt, int tile, const RunArgs& a, hipStream_t st);
 bool big_tile_takes(int fmt, const RunArgs& a);
 hipError_t launch_mfma_big(int fmt, const RunArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// zr = the bf16 planes [R_hi | R_lo] of the group row sums of a.A (rows of a.K fp16
+// values, scale groups of a.group_size positions, or one group when it is negative)
+// for the zero-point folding of the 256 x 256 tiles; a.K / 32 <= ROWSUM_MAX_UNITS
+constexpr int ROWSUM_MAX_UNITS = 8192;
+hipError_t launch_group_rowsum(const RunArgs& a, uint16_t* zr, hipStream_t st);
+// zp = the bf16 planes [P_hi | P_lo] of P = -s z for each of the Npad columns, from the
+// (scale, zero) pairs a.S ([zr_G][Npad])
+hipError_t launch_zero_planes(const RunArgs& a, uint16_t* zp, hipStream_t st);
 // dst[m, k] = k < K ? A[m, k] : 0 for rows of Kpad elements of esz bytes (Kpad * esz a
 // multiple of 16, dst 16-byte aligned; A any alignment of its element size)
 hipError_t launch_pad_rows(const void* A, void* dst, int64_t M, int64_t K, int64_t Kpad, int esz,

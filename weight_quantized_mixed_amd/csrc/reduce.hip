@@ -3,7 +3,9 @@
 // outputs with a bias, its filling with the bias rows; the fp32 -> fp16
 // conversion after atomic accumulation, and the fixed-order two-pass reduction
 // of per-part partials (the deterministic alternative to the atomic reduction
-// of hidet issue #364's parallel-k), each adding the bias if there is one.
+// of hidet issue #364's parallel-k), each adding the bias if there is one; the
+// activation row sums by scale group that fold uint4 zero points out of the
+// large tiles' K loop.
 #include "qgemm_internal.hpp"
 
 namespace qg {
@@ -65,6 +67,95 @@ __global__ void pad_rows_kernel(const T* __restrict__ A, uint4* __restrict__ dst
   }
 }
 
+// fp32 -> bf16, rounded to nearest even (finite values)
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// sum of the 8 fp16 values of a 16-byte chunk in fp32, in position order
+__device__ __forceinline__ float sum8_f16(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+    s += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+  }
+  return s;
+}
+
+// Row sums of A over the scale groups (zero-point folding of the 256 x 256 tiles):
+// one workgroup per row.  A lane sums a 16-byte chunk (8 positions) in fp32, four
+// neighbouring lanes combine theirs into the sum of a 32-position unit by a fixed
+// butterfly, so every run rounds alike, and after a barrier lane g adds the units of
+// group g in order.  Row length K (a multiple of 32, at most 32 * ROWSUM_MAX_UNITS);
+// units: K / 32 floats of dynamic LDS.
+constexpr int ROWSUM_BATCH = 4;  // chunks per lane in flight
+__global__ __launch_bounds__(256) void group_rowsum_kernel(const uint4* __restrict__ A, uint16_t* __restrict__ zr,
+                                                           int K, int upg, int G, int gp) {
+  extern __shared__ float unit[];
+  const int chunks = K / 8;
+  const uint4* row = A + (size_t)blockIdx.x * chunks;
+  for (int c0 = 0; c0 < chunks; c0 += 256 * ROWSUM_BATCH) {
+    uint4 v[ROWSUM_BATCH];
+#pragma unroll
+    for (int b = 0; b < ROWSUM_BATCH; ++b) {
+      const int c = c0 + b * 256 + (int)threadIdx.x;
+      v[b] = c < chunks ? row[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < ROWSUM_BATCH; ++b) {
+      // chunks is a multiple of 4, so the four lanes of a unit are all in range or all out
+      const int c = c0 + b * 256 + (int)threadIdx.x;
+      float s = sum8_f16(v[b]);
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (c < chunks && (threadIdx.x & 3) == 0) unit[c >> 2] = s;
+    }
+  }
+  __syncthreads();
+  uint16_t* out = zr + (size_t)blockIdx.x * 2 * gp;
+  for (int g = threadIdx.x; g < gp; g += 256) {
+    float r = 0.f;
+    if (g < G)
+      for (int u = g * upg; u < (g + 1) * upg; ++u) r += unit[u];
+    const uint16_t hi = bf16_rne(r);
+    out[g] = hi;
+    out[gp + g] = bf16_rne(r - __uint_as_float((uint32_t)hi << 16));
+  }
+}
+
+// The zero-point term of the 256 x 256 tiles for each column and scale group, as bf16
+// hi + lo planes, [Npad][hi gp | lo gp], from the (scale, zero) pairs [G][Npad]; groups
+// G .. gp - 1 zero.  Those tiles upcast a weight q of the group as one fp16 fma,
+// (1024 + q) s + c with b = fp16(1024 + z) = 1024 + r and c = fp16(-b s), which is
+// (q - r) s + d rounded once, d = c + b s (exact in fp32, as is b s); the term is
+// P = -(z - r) s - d, so that adding sum_g R[m, g] P[g, n] leaves (q - z) s.
+// Consecutive threads take consecutive columns of one group, so the pairs are read
+// in order.
+__global__ void zero_planes_kernel(const uint32_t* __restrict__ S, uint16_t* __restrict__ zp, int Npad, int G,
+                                   int gp) {
+  const int64_t total = (int64_t)Npad * gp;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int g = (int)(i / Npad), col = (int)(i - (int64_t)g * Npad);
+    float p = 0.f;
+    if (g < G) {
+      const uint32_t u = S[(size_t)g * Npad + col];
+      const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+      const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+      const float b = (float)(_Float16)(z + 1024.f);  // z + 1024 is exact in fp32
+      const float bs = b * s;                         // exact: 11 x 11 significant bits
+      const float d = (float)(_Float16)(-bs) + bs;    // the rounding of c, exact
+      p = -(z - (b - 1024.f)) * s - d;
+    }
+    const uint16_t hi = bf16_rne(p);
+    uint16_t* o = zp + (size_t)col * 2 * gp + g;
+    o[0] = hi;
+    o[gp] = bf16_rne(p - __uint_as_float((uint32_t)hi << 16));
+  }
+}
+
 int grid_for(size_t items, int threads) {
   size_t b = (items + threads - 1) / threads;
   if (b > 8192) b = 8192;
@@ -92,6 +183,22 @@ hipError_t launch_pad_rows(const void* A, void* dst, int64_t M, int64_t K, int64
   else
     hipLaunchKernelGGL(pad_rows_kernel<uint8_t>, dim3(grid_for(chunks, 256)), dim3(256), 0, st,
                        static_cast<const uint8_t*>(A), static_cast<uint4*>(dst), M, K, Kpad);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_rowsum(const RunArgs& a, uint16_t* zr, hipStream_t st) {
+  if (a.K % 32 != 0 || a.K / 32 > ROWSUM_MAX_UNITS || a.zr_gp % 32 != 0 || a.zr_G > a.zr_gp)
+    return hipErrorInvalidValue;
+  const int upg = a.group_size > 0 ? a.group_size / 32 : a.K / 32;
+  hipLaunchKernelGGL(group_rowsum_kernel, dim3(a.M), dim3(256), (size_t)(a.K / 32) * sizeof(float), st,
+                     static_cast<const uint4*>(a.A), zr, a.K, upg, a.zr_G, a.zr_gp);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_planes(const RunArgs& a, uint16_t* zp, hipStream_t st) {
+  if (!a.S || a.zr_gp % 32 != 0 || a.zr_G > a.zr_gp) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_planes_kernel, dim3(grid_for((size_t)a.Npad * a.zr_gp, 256)), dim3(256), 0, st,
+                     static_cast<const uint32_t*>(a.S), zp, a.Npad, a.zr_G, a.zr_gp);
   return hipGetLastError();
 }
 
