@@ -79,6 +79,7 @@ struct BigGeo {
   static_assert(B_BYTES % 4096 == 0, "B slots split evenly over the waves");
   static_assert(NSTAGE >= 2 && (NSTAGE - 1) * L < 64, "ring depth and the 6-bit load counter");
   static_assert(!SCALED || (FMT == FMT_I4 || FMT == FMT_U4), "scales only with int4 weights");
+  static_assert(!SCALED || KB == 2 * SPOS, "a scaled superblock is two stages (scales read on even stages)");
 };
 
 template <int FMT, bool SCALED, bool ZEROS>
@@ -226,14 +227,17 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
       const int r = wm * 128 + i * 16 + l16;
       f.a[i] = *reinterpret_cast<const uint4*>(base + r * ROWB + swz<ROWB, PACKED>(r, chunk) * 16);
     };
-    auto read_b = [&](Frag& f, const uint8_t* base, auto T, auto J) {
+    // SCL: the stage's scales are read as well (at step 0 of a stage whose scales may
+    // differ from the previous stage's)
+    auto read_b = [&](Frag& f, const uint8_t* base, auto T, auto J, auto SCL) {
       constexpr int t = decltype(T)::value, j = decltype(J)::value;
+      constexpr bool scl = decltype(SCL)::value;
       const uint8_t* lb = base + A_BYTES + (wn * 8 + j) * BSB;
       if constexpr (PACKED)
         rw[j] = *reinterpret_cast<const uint32_t*>(lb + ((q & 1) * 16 + l16) * 16 + (2 * t + (q >> 1)) * 4);
       else
         f.b[j] = *reinterpret_cast<const uint4*>(lb + t * 1024 + lane * 16);  // superblock t, piece = lane
-      if constexpr (SCALED && t == 0) {
+      if constexpr (SCALED && t == 0 && scl) {
         const int col = (wn * 8 + j) * 16 + l16;
         // with zero points the slot holds (scale, zero) pairs; the zero points are
         // applied after the loop
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
     // the matrix core idle); the reads of step T of the slot at rb into nxt, after
     // every other MFMA of the first half; and nxt's upcasts in the second half.
     constexpr int NR = 16, NU = PACKED ? 32 : 0;
-    auto step = [&](const Frag& cur, Frag& nxt, const uint8_t* rb, auto T, auto DMA) {
+    auto step = [&](const Frag& cur, Frag& nxt, const uint8_t* rb, auto T, auto DMA, auto SCL) {
       constexpr bool D = decltype(DMA)::value;
       constexpr int ND = D ? L : 0;
       constexpr int DSTEP = ND > 0 ? QG_BIG_DSPAN / ND : 64;  // loads over the first DSPAN MFMAs
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
           fence();
         }
         if constexpr (k % RS == 1 % RS && k / RS < 8) {
-          read_b(nxt, rb, T, std::integral_constant<int, k / RS>{});
+          read_b(nxt, rb, T, std::integral_constant<int, k / RS>{}, SCL);
           fence();
         } else if constexpr (k % RS == 1 % RS && k / RS < NR) {
           read_a(nxt, rb, T, std::integral_constant<int, k / RS - 8>{});
@@ -347,23 +351,36 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
     wait_vmcnt<(NSTAGE - 1) * L>();
     asm volatile("s_barrier" ::: "memory");
     Frag X, Y;
-    static_for(std::make_integer_sequence<int, 8>{}, [&](auto J) { read_b(X, slot(0), I0{}, J); });
+    static_for(std::make_integer_sequence<int, 8>{}, [&](auto J) { read_b(X, slot(0), I0{}, J, std::true_type{}); });
     static_for(std::make_integer_sequence<int, 8>{}, [&](auto I) { read_a(X, slot(0), I0{}, I); });
     static_for(std::make_integer_sequence<int, 8>{}, [&](auto J) {
       static_for(std::make_integer_sequence<int, 4>{}, [&](auto JJ) { make_b_part(X, J, JJ); });
     });
 
-    for (int s = 0; s < nst; ++s) {
-      // step 0 of stage s; read step 1 of the same slot
-      step(X, Y, slot(s), I1{}, std::false_type{});
-      // stage s + 1 landed (this wave's loads, then every wave's), and every wave's
-      // reads of slot s are done: slot s takes stage s + NSTAGE
-      wait_vm_lgkm0<(NSTAGE - 2) * L>();
-      asm volatile("s_barrier" ::: "memory");
-      // step 1 of stage s; issue stage s + NSTAGE, read step 0 of stage s + 1 (past
-      // the last stage: copies that are never used)
-      step(Y, X, slot(s + 1), I0{}, std::true_type{});
+    // One stage: step 0 on X (reading step 1 of the same slot into Y); when stage s + 1
+    // has landed (this wave's loads, then every wave's) and every wave's reads of slot
+    // s are done, a barrier; step 1 on Y, which issues stage s + NSTAGE into slot s
+    // and reads step 0 of stage s + 1 into X (its scales when SCL; past the last
+    // stage: copies that are never used).
+#define QG_BIG_STAGE(s, SCL)                                                    \
+  do {                                                                          \
+    step(X, Y, slot(s), I1{}, std::false_type{}, std::false_type{});          \
+    wait_vm_lgkm0<(NSTAGE - 2) * L>();                                        \
+    asm volatile("s_barrier" ::: "memory");                                   \
+    step(Y, X, slot((s) + 1), I0{}, std::true_type{}, SCL{});                 \
+  } while (0)
+    if constexpr (SCALED) {
+      // Scaled int4 groups are whole superblocks (or all of K), two stages each, and a
+      // part starts on a group: the scales change only at even stages of the part,
+      // whose count is even, so odd stages keep the registers of the stage before.
+      for (int s = 0; s < nst; s += 2) {
+        QG_BIG_STAGE(s, std::false_type);
+        QG_BIG_STAGE(s + 1, std::true_type);
+      }
+    } else {
+      for (int s = 0; s < nst; ++s) QG_BIG_STAGE(s, std::true_type);
     }
+#undef QG_BIG_STAGE
     wait_vmcnt<0>();  // drain the tail copies before the workgroup's LDS is released
   }
   if constexpr (ZEROS) {
