@@ -32,6 +32,7 @@ CASES = [
     (4, 1000, 1024, "i4", 0, False, 1, "-"),           # no split: no scratch at all
     (8, 1000, 4104, "i4", 0, False, 3, "atomic"),      # K padded: activation rows in scratch too
     (40, 264, 4100, "i8", 0, False, 1, "-"),           # K padded, no split
+    (4100, 3836, 512, "u4", 128, True, 1, "-"),        # 256 x 256 tiles: zero-point planes in scratch
 ]
 
 
