@@ -47,6 +47,12 @@ using namespace dl;
 #ifndef QG_BIG_MAXST
 #define QG_BIG_MAXST 4
 #endif
+// ring depth of the scaled int4 kernel, whose loop runs two stages per iteration: an
+// even depth keeps each unrolled stage on a fixed slot, so its LDS addresses are
+// constants
+#ifndef QG_BIG_MAXST_SCALED
+#define QG_BIG_MAXST_SCALED 2
+#endif
 #ifndef QG_BIG_U0
 #define QG_BIG_U0 16
 #endif
@@ -70,7 +76,8 @@ struct BigGeo {
   static constexpr int S_BYTES = SCALED ? 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
   static constexpr int FIT = 160 * 1024 / STAGE;
-  static constexpr int NSTAGE = FIT < QG_BIG_MAXST ? FIT : QG_BIG_MAXST;
+  static constexpr int MAXST = SCALED ? QG_BIG_MAXST_SCALED : QG_BIG_MAXST;
+  static constexpr int NSTAGE = FIT < MAXST ? FIT : MAXST;
   // direct loads of a wave per stage: slots wave, wave + 4, ... of A and of B,
   // and a quarter of the scale slot
   static constexpr int LA = A_BYTES / 1024 / 4, LB = B_BYTES / 1024 / 4;
