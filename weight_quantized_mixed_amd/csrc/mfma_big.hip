@@ -1,7 +1,7 @@
 // Large-tile matrix-core path for fp16 and int4 / uint4 weights: 256 x 256 output
 // tiles computed by four waves, each owning a 128 x 128
 // quadrant (64 MFMA tiles of 16 x 16, whose accumulators live in the accumulation
-// registers), from a ring of 2 to 4 LDS stages that global_load_lds_dwordx4 fills
+// registers), from a ring of two LDS stages that global_load_lds_dwordx4 fills
 // straight from memory.  This is the shape of the large-M products in the BitBLAS
 // issue #252 benchmark table (M = 16384 rows): every fragment read from LDS feeds 8
 // MFMAs, so a wave reads 64 KiB of fragments per 32 positions of a tile instead of
@@ -44,14 +44,12 @@ using namespace dl;
 #ifndef QG_BIG_GROUP_M
 #define QG_BIG_GROUP_M 2
 #endif
+// LDS ring depth (stages in flight + 1).  The int4 loop runs two stages per iteration,
+// and a depth of two keeps each of them on a fixed slot, so their fragment addresses
+// are constants (a depth of three or four recomputed them: 16384^3 uint4 g = 128 6.84 ->
+// 6.53 ms, int4 unscaled 6.03-6.06 -> 5.88-5.89 ms); fp16 stages (64 KiB) fit only two.
 #ifndef QG_BIG_MAXST
-#define QG_BIG_MAXST 4
-#endif
-// ring depth of the scaled int4 kernel, whose loop runs two stages per iteration: an
-// even depth keeps each unrolled stage on a fixed slot, so its LDS addresses are
-// constants
-#ifndef QG_BIG_MAXST_SCALED
-#define QG_BIG_MAXST_SCALED 2
+#define QG_BIG_MAXST 2
 #endif
 #ifndef QG_BIG_U0
 #define QG_BIG_U0 16
@@ -76,8 +74,7 @@ struct BigGeo {
   static constexpr int S_BYTES = SCALED ? 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
   static constexpr int FIT = 160 * 1024 / STAGE;
-  static constexpr int MAXST = SCALED ? QG_BIG_MAXST_SCALED : QG_BIG_MAXST;
-  static constexpr int NSTAGE = FIT < MAXST ? FIT : MAXST;
+  static constexpr int NSTAGE = FIT < QG_BIG_MAXST ? FIT : QG_BIG_MAXST;
   // direct loads of a wave per stage: slots wave, wave + 4, ... of A and of B,
   // and a quarter of the scale slot
   static constexpr int LA = A_BYTES / 1024 / 4, LB = B_BYTES / 1024 / 4;
@@ -86,7 +83,7 @@ struct BigGeo {
   static_assert(B_BYTES % 4096 == 0, "B slots split evenly over the waves");
   static_assert(NSTAGE >= 2 && (NSTAGE - 1) * L < 64, "ring depth and the 6-bit load counter");
   static_assert(!SCALED || (FMT == FMT_I4 || FMT == FMT_U4), "scales only with int4 weights");
-  static_assert(!SCALED || KB == 2 * SPOS, "a scaled superblock is two stages (scales read on even stages)");
+  static_assert(!PACKED || FMT == FMT_I2 || KB == 2 * SPOS, "an int4 superblock is two stages (two per iteration)");
 };
 
 template <int FMT, bool SCALED, bool ZEROS>
@@ -376,10 +373,11 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
     asm volatile("s_barrier" ::: "memory");                                   \
     step(Y, X, slot((s) + 1), I0{}, std::true_type{}, SCL{});                 \
   } while (0)
-    if constexpr (SCALED) {
-      // Scaled int4 groups are whole superblocks (or all of K), two stages each, and a
-      // part starts on a group: the scales change only at even stages of the part,
-      // whose count is even, so odd stages keep the registers of the stage before.
+    if constexpr (I4) {
+      // int4: a superblock is two stages and a part is whole superblocks, so the loop
+      // takes two stages per iteration.  Scale groups are whole superblocks (or all of
+      // K): the scales change only at even stages of the part, and odd stages keep the
+      // registers of the stage before.
       for (int s = 0; s < nst; s += 2) {
         QG_BIG_STAGE(s, std::false_type);
         QG_BIG_STAGE(s + 1, std::true_type);
