@@ -445,26 +445,41 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = m0 + wm * 128 + i * 16 + q * 4 + r;
-          if (row < a.M && col < a.N) f(row, col, (size_t)row * a.N + col, acc[i][j][r]);
+          if (row < a.M && col < a.N) f(row, j, (size_t)row * a.N + col, acc[i][j][r]);
         }
       }
   };
-  auto epi = [&](int col) { return a.epi_scale ? (float)a.epi_scale[col] : 1.f; };
+  // The per-column values of this lane's 8 columns (epilogue scale, bias, int8 column
+  // scale) are read before any store: C is written through pointers of the types of
+  // those arrays, so read between the stores each read would wait behind the stores
+  // before it.
+  float es[8], bf[8], cs[8];
+  int bi[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int col = n0 + wn * 128 + j * 16 + l16;
+    const bool in = col < a.N;
+    es[j] = FP && a.epi_scale && in ? (float)a.epi_scale[col] : 1.f;
+    bf[j] = (FP || a.row_scale) && in ? bias_f(a, col) : 0.f;  // fp16 outputs: fp16 bias
+    bi[j] = !FP && !a.row_scale && in ? bias_i(a, col) : 0;
+    cs[j] = !FP && a.row_scale && in ? a.col_scale[col] : 0.f;
+  }
   if (a.out_mode == OUT_STORE) {
     if constexpr (FP)
-      each([&](int, int col, size_t o, float v) {
-        static_cast<_Float16*>(a.C)[o] = (_Float16)(v * epi(col) + bias_f(a, col));
-      });
+      each([&](int, int j, size_t o, float v) { static_cast<_Float16*>(a.C)[o] = (_Float16)(v * es[j] + bf[j]); });
     else if (a.row_scale)
-      each([&](int row, int col, size_t o, int v) { static_cast<_Float16*>(a.C)[o] = dq_out(a, row, col, v); });
+      each([&](int row, int j, size_t o, int v) {  // as dq_out, with the column values above
+        static_cast<_Float16*>(a.C)[o] = (_Float16)((float)v * a.row_scale[row] * cs[j] + bf[j]);
+      });
     else
-      each([&](int, int col, size_t o, int v) { static_cast<int*>(a.C)[o] = v + bias_i(a, col); });
+      each([&](int, int j, size_t o, int v) { static_cast<int*>(a.C)[o] = v + bi[j]; });
   } else if (a.out_mode == OUT_ATOMIC) {
-    if constexpr (FP) each([&](int, int col, size_t o, float v) { unsafeAtomicAdd(static_cast<float*>(a.ws) + o, v * epi(col)); });
+    if constexpr (FP)
+      each([&](int, int j, size_t o, float v) { unsafeAtomicAdd(static_cast<float*>(a.ws) + o, v * es[j]); });
     else each([&](int, int, size_t o, int v) { atomicAdd(int_atomic_target(a) + o, v); });
   } else {
     const size_t po = (size_t)part * a.M * a.N;
-    if constexpr (FP) each([&](int, int col, size_t o, float v) { static_cast<float*>(a.ws)[po + o] = v * epi(col); });
+    if constexpr (FP) each([&](int, int j, size_t o, float v) { static_cast<float*>(a.ws)[po + o] = v * es[j]; });
     else each([&](int, int, size_t o, int v) { static_cast<int*>(a.ws)[po + o] = v; });
   }
 }

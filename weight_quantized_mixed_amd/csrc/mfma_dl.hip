@@ -687,16 +687,29 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
         for (int j = 0; j < WTN; ++j) acc[i][j] += red[(g - 1) * G::RED + ((wl * WTM + i) * WTN + j) * 64 + lane];
   }
 
-  // epilogue: lane l holds rows 4 (l / 16) + r, column l % 16 of each 16 x 16 sub-tile
+  // epilogue: lane l holds rows 4 (l / 16) + r, column l % 16 of each 16 x 16 sub-tile.
+  // The per-column values (bias, epilogue scale, int8 column scale) are read before any
+  // store: C is written through pointers of the types of those arrays, so read between
+  // the stores each read would wait behind the stores before it.
+  float bfv[WTN], esv[WTN], csv[WTN];
+  int biv[WTN];
+#pragma unroll
+  for (int j = 0; j < WTN; ++j) {
+    const int col = n0 + (wn * WTN + j) * 16 + l16;
+    const bool st = col < a.N && a.out_mode == OUT_STORE;
+    bfv[j] = (FP || a.row_scale) && st ? bias_f(a, col) : 0.f;  // fp16 outputs: fp16 bias
+    biv[j] = !FP && !a.row_scale && st ? bias_i(a, col) : 0;
+    csv[j] = !FP && a.row_scale && st ? a.col_scale[col] : 0.f;
+    esv[j] = FP && a.epi_scale && col < a.N ? (float)a.epi_scale[col] : 1.f;
+  }
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int col = n0 + (wn * WTN + j) * 16 + l16;
       if (col >= a.N) continue;
-      const float bf = FP && a.out_mode == OUT_STORE ? bias_f(a, col) : 0.f;
-      const int bi = !FP && a.out_mode == OUT_STORE ? bias_i(a, col) : 0;
-      const float es = FP && a.epi_scale ? (float)a.epi_scale[col] : 1.f;
+      const float bf = bfv[j], es = esv[j];
+      const int bi = biv[j];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + (wm * WTM + i) * 16 + q * 4 + r;
@@ -706,7 +719,8 @@ __global__ __launch_bounds__(G::NWT * 64) void mfma_dl_kernel(RunArgs a) {
         if constexpr (FP) v *= es;
         if (a.out_mode == OUT_STORE) {
           if constexpr (FP) static_cast<_Float16*>(a.C)[o] = (_Float16)(v + bf);
-          else if (a.row_scale) static_cast<_Float16*>(a.C)[o] = dq_out(a, row, col, v);
+          else if (a.row_scale)  // as dq_out, with the column values above
+            static_cast<_Float16*>(a.C)[o] = (_Float16)((float)v * a.row_scale[row] * csv[j] + bf);
           else static_cast<int*>(a.C)[o] = v + bi;
         } else if (a.out_mode == OUT_ATOMIC) {
           if constexpr (FP) unsafeAtomicAdd(static_cast<float*>(a.ws) + o, v);
