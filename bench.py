@@ -303,7 +303,9 @@ GRID = ([{"w": "i4", "M": M, "N": 16384, "K": 16384, "g": 128} for M in (32, 128
         + [{"w": "f16", "M": 16384, "N": 16384, "K": 16384},
            {"w": "u4", "M": 16384, "N": 16384, "K": 16384, "g": 128, "zeros": True}]
         + [{"w": "i4", "M": 16384, "N": 16384, "K": 16384, "g": g} for g in (0, -1)]
-        + [{"w": w, "M": 16384, "N": 16384, "K": 16384} for w in ("i8", "i2")])
+        + [{"w": w, "M": 16384, "N": 16384, "K": 16384} for w in ("i8", "i2")]
+        # W4A16 with g = 128 scales at M = 16384, the last M of the pages' grid
+        + [{"w": "i4", "M": 16384, "N": 16384, "K": 16384, "g": 128}])
 
 
 # the timed workload: W4A16 decode at M = 1, N = K = 16384, g = 128, k_parts = 1
