@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
     auto step = [&](const Frag& cur, Frag& nxt, const uint8_t* rb, auto T, auto DMA, auto SCL) {
       constexpr bool D = decltype(DMA)::value;
       constexpr int ND = D ? L : 0;
-      constexpr int DSTEP = ND > 0 ? QG_BIG_DSPAN / ND : 64;  // loads over the first DSPAN MFMAs
+      constexpr int DSTEP = ND > 0 ? QG_BIG_DSPAN / (ND > 0 ? ND : 1) : 64;  // loads over the first DSPAN MFMAs
       constexpr int U0 = QG_BIG_U0;    // first MFMA followed by an upcast
       constexpr int RS = QG_BIG_RSTEP; // MFMAs between two fragment reads
       fence();
