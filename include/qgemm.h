@@ -116,11 +116,12 @@ typedef enum {
  *                 of 32.  Other weight formats require 0.
  *   has_zeros     0 or 1; 1 only with w_dtype U4 and group_size != 0.
  *                 Scales of U4 weights: |s| < 64, and with zero points
- *                 |s| * (1024 + z) < 65504 with 0 <= z < 1024 for rows that take
- *                 the 256 x 256 tiles (large M): those tiles upcast and scale a
- *                 weight with one fp16 fma whose addend, -1024 s or
- *                 -fp16(1024 + z) s, must be finite (BitBLAS issue #252, the
- *                 uint4 op configs with scaling and zero points).
+ *                 |s| * (1024 + z) < 65504 with 0 <= z < 1024; of I4 weights
+ *                 with g > 0: |s| < 63; for rows that take the 256 x 256 tiles
+ *                 (large M): those tiles upcast and scale a weight with one
+ *                 fp16 fma whose addend, -1024 s, -fp16(1024 + z) s or -1032 s,
+ *                 must be finite (BitBLAS issue #252, the int4 / uint4 op
+ *                 configs with scaling and zero points).
  *   k_parts       >= 1: number of contiguous, group-aligned K ranges computed by
  *                 separate workgroups and reduced with fp32/int32 global atomics
  *                 (default) or by ordered partials and one summing pass
@@ -140,12 +141,14 @@ typedef enum {
  *                 superblocks (or none): 4 parts for runs of 17 rows or more when the
  *                 plan has more than 16 rows, else 2 parts for runs of 9 or more.
  *                 U4 with zero points and groups that are whole multiples of 128
- *                 (or one group over K), plans of more than 128 rows: the zero
- *                 points of the 256 x 256 tiles are applied after their K loop
- *                 as sum_g R[m, g] P[g, n], with R the row sums of A over each
- *                 group and P from the scales and zeros (each held as two bf16
- *                 planes of roundup(G, 32) values per row of A and per padded
- *                 column); the workspace then ends with those planes.
+ *                 (or one group over K), and I4 with such groups (its offset 8
+ *                 as the zero point): runs that take the 256 x 256 tiles apply
+ *                 the zero points after their K loop as sum_g R[m, g] P[g, n],
+ *                 with R the row sums of A over each group and P from the scales
+ *                 and zeros (each held as two bf16 planes of roundup(G, 32)
+ *                 values per row of A and per padded column); the workspace then
+ *                 ends with those planes, sized for the largest run of the plan
+ *                 that takes those tiles.
  */
 qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K,
                           qgemm_dtype a_dtype, qgemm_dtype w_dtype, qgemm_dtype out_dtype,
@@ -221,8 +224,8 @@ qgemm_status qgemm_run_ex(const qgemm_plan* plan, int64_t M, const void* A, cons
  * library runs on holds until the process ends; this call itself allocates
  * nothing.  It needs the workspace that qgemm_run_ex would for run-time M (the
  * atomic accumulator or the two-pass partials, plus the zero-padded activation
- * rows when K is not a whole number of blocks, plus the zero-point planes of U4
- * plans with zero points on the 256 x 256 tiles; none for an unsplit plan of
+ * rows when K is not a whole number of blocks, plus the zero-point planes of U4 /
+ * I4 plans on the 256 x 256 tiles; none for an unsplit plan of
  * whole blocks otherwise); more than the maximum returns QGEMM_ERR_UNSUPPORTED
  * before any device call.
  * Every call on one GPU shares that GPU's scratch: calls that may overlap in

@@ -107,12 +107,16 @@ def test_sizes_and_paths():
     plan, pb, wb = _create(M=9, N=100, k_parts=4, flags=q.QGEMM_SPLIT_AUTO)
     assert wb == 4 * 9 * 100 * 4                            # auto: fp16 outputs take the partials
     q.qgemm_destroy(plan)
+    # int4 with g = 128 on the 256 x 256 tiles: the workspace ends with the planes of the
+    # offset folding (row sums of A over 32 groups for each row, the per-column term for
+    # each of the 8448 padded columns; two bf16 planes of 32 values each)
+    fold = (4100 + 8448) * 32 * 2 * 2
     plan, pb, wb = _create(M=4100, N=8400, K=4096, k_parts=2, flags=q.QGEMM_SPLIT_AUTO)
-    assert wb == 4100 * 8400 * 4                            # ... until they pass 256 MiB
+    assert wb == 4100 * 8400 * 4 + fold                     # ... until they pass 256 MiB
     q.qgemm_destroy(plan)
     plan, pb, wb = _create(M=4100, N=8400, K=4096, k_parts=2,
                            flags=q.QGEMM_DETERMINISTIC | q.QGEMM_SPLIT_AUTO)
-    assert wb == 2 * 4100 * 8400 * 4                        # deterministic: partials regardless
+    assert wb == 2 * 4100 * 8400 * 4 + fold                 # deterministic: partials regardless
     q.qgemm_destroy(plan)
     i8 = dict(a_dtype="i8", w_dtype="i8", out_dtype="i32", accum_dtype="i32", group_size=0)
     plan, pb, wb = _create(k_parts=4, **i8)
@@ -260,7 +264,7 @@ def test_noalloc_rejects_before_any_device_call():
     big, _, wb = _create(M=4096, N=16384, K=4096, k_parts=2)   # fp32 atomics: 256 MiB of scratch
     dq, _, _ = _create(a_dtype="i8", w_dtype="i8", out_dtype="f16", accum_dtype="i32", group_size=0, M=4)
     try:
-        assert wb == 4096 * 16384 * 4
+        assert wb == 4096 * 16384 * 4 + (4096 + 16384) * 32 * 2 * 2   # and the int4 folding's planes
         with pytest.raises(q.QGemmError) as e:
             q.qgemm_run_noalloc(big, 4096, 16, 16, 0, 16, 0)
         assert e.value.status == q.QGEMM_ERR_UNSUPPORTED
@@ -329,11 +333,7 @@ def test_library_splits_long_int4_tiles_itself():
         (dict(M=128, N=8192, K=8192), 4 * 128 * 8192 * 4),     # 64 tiles: four
         (dict(M=128, N=4096, K=11008), 8 * 128 * 4096 * 4),    # 32 tiles: eight
         (dict(M=40, N=4096, K=8192), 8 * 40 * 4096 * 4),
-        # uint4 with zero points from 129 rows: also the row sums and the -s z columns
-        # that runs of fewer rows on the 256 x 256 tiles would need (two bf16 planes of
-        # one group padded to 32 for each row and each of the 4096 columns)
-        (dict(M=256, N=4096, K=11008, group_size=-1, w_dtype="u4", has_zeros=1),
-         4 * 256 * 4096 * 4 + (256 + 4096) * 32 * 2 * 2),
+        (dict(M=256, N=4096, K=11008, group_size=-1, w_dtype="u4", has_zeros=1), 4 * 256 * 4096 * 4),
         # 9..32 rows at N <= 4096 (the matrix-core GEMV): four parts from 17 rows, two below
         (dict(M=32, N=4096, K=11008), 4 * 32 * 4096 * 4),
         (dict(M=20, N=2048, K=8192, group_size=-1), 4 * 20 * 2048 * 4),

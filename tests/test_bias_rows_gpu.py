@@ -57,7 +57,9 @@ def test_bias_with_atomic_split(w_dtype, g):
     M, N, K = 4100, 8400, 256
     say(f"case bias atomic split M={M} N={N} K={K} {w_dtype} kp=2")
     c = Case(M, N, K, w_dtype, g, False, k_parts=2, seed=5100, split_auto=True)
-    assert c.q.ws_bytes == (M * N * 4 if w_dtype == "i4" else 0)
+    # int4 on the 256 x 256 tiles adds the folding's planes (row sums over K / g = 2 groups
+    # padded to 32, the per-column term for the 8448 padded columns)
+    assert c.q.ws_bytes == (M * N * 4 + (M + 8448) * 32 * 2 * 2 if w_dtype == "i4" else 0)
     b = _bias(c, 5101)
     rng = np.random.default_rng(4)
     rows = np.unique(np.concatenate([rng.choice(M, 150, replace=False), [0, M - 1]]))

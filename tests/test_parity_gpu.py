@@ -205,11 +205,13 @@ BIG = [
     (4096, 4096, 512, "u4", 256, False),
     (4096, 4096, 384, "i4", -1, False),
     (4096, 4096, 256, "i4", 0, False),
-    # uint4 with zero points folded out of the K loop (255 tiles of 256 x 256 fill the
-    # CUs at k_parts 1 as well): one group over K (with a K tail read zero-padded),
-    # groups of three superblocks
+    # uint4 with zero points and int4 with scale groups, folded out of the K loop (255
+    # tiles of 256 x 256 fill the CUs at k_parts 1 as well): one group over K (with a K
+    # tail read zero-padded), groups of three superblocks
     (4100, 3836, 1000, "u4", -1, True),
     (4100, 3836, 768, "u4", 384, True),
+    (4100, 3836, 512, "i4", 128, False),
+    (4100, 3836, 768, "i4", 384, False),
 ]
 
 
@@ -232,10 +234,11 @@ def test_big_tile_parity(M, N, K, w_dtype, g, zeros, kp, det):
 # columns: 255 tiles, 2900 rows: 180, both on 256 x 256 tiles), and activations whose
 # group sums pass the fp16 range (a constant 1000: R = 128000 per group; scales 2^-6,
 # so that both sides are exact up to the fp32 sums and any overflow of R shows).
-def test_zero_fold_bias_fewer_rows_and_large_sums():
+@pytest.mark.parametrize("w_dtype,zeros", [("u4", True), ("i4", False)])
+def test_zero_fold_bias_fewer_rows_and_large_sums(w_dtype, zeros):
     M, N, K = 4100, 3836, 512
-    say(f"zero fold M={M} N={N} K={K} u4 g=128 zeros: bias, fewer rows, large sums")
-    c = Case(M, N, K, "u4", 128, True, seed=91)
+    say(f"zero fold M={M} N={N} K={K} {w_dtype} g=128 zeros={zeros}: bias, fewer rows, large sums")
+    c = Case(M, N, K, w_dtype, 128, zeros, seed=91)
     b = synth.draw_bias(N, "f16", 92)
     rng = np.random.default_rng(93)
     cols = np.unique(np.concatenate([rng.choice(N, 300, replace=False), [0, 255, 256, N - 1]]))
@@ -246,11 +249,11 @@ def test_zero_fold_bias_fewer_rows_and_large_sums():
         assert_matches(gpu[np.ix_(rows, cols)], c.reference(rows=rows, cols=cols, bias=b),
                        f"zero fold bias M={m}")
     M, N = 4096, 4096
-    p = synth.make_problem(M, N, K, "u4", group_size=128, has_zeros=True, seed=94)
-    big = synth.make_problem(M, N, K, "u4", group_size=128, has_zeros=True, seed=94,
+    p = synth.make_problem(M, N, K, w_dtype, group_size=128, has_zeros=zeros, seed=94)
+    big = synth.make_problem(M, N, K, w_dtype, group_size=128, has_zeros=zeros, seed=94,
                              A=np.full((M, K), 1000, dtype=np.float16), q=p.q,
                              s=np.full_like(p.s, 2.0 ** -6), z=p.z)
-    c2 = Case(M, N, K, "u4", 128, True, problem=big)
+    c2 = Case(M, N, K, w_dtype, 128, zeros, problem=big)
     rows = np.unique(np.concatenate([rng.choice(M, 100, replace=False), [0, M - 1]]))
     cols = np.unique(np.concatenate([rng.choice(N, 300, replace=False), [0, N - 1]]))
     gpu = c2.run()
@@ -264,10 +267,11 @@ def test_atomic_split_past_the_partials_cap(w_dtype, g, zeros):
     M, N, K = 4100, 8400, 256
     say(f"atomic split M={M} N={N} K={K} {w_dtype} g={g} zeros={zeros} kp=2")
     c = Case(M, N, K, w_dtype, g, zeros, k_parts=2, seed=M + N + 17)
-    # uint4 with zero points on the 256 x 256 tiles: after the accumulator, the two bf16
-    # planes of the row sums over the scale groups (K / g = 2, padded to 32 per plane)
-    # and those of -s z for the 8448 padded columns
-    zr = (M + 8448) * 32 * 2 * 2 if zeros else 0
+    # uint4 with zero points and int4 with scale groups on the 256 x 256 tiles: after
+    # the accumulator, the two bf16 planes of the row sums over the scale groups (K / g
+    # = 2, padded to 32 per plane) and those of the per-column term for the 8448 padded
+    # columns
+    zr = (M + 8448) * 32 * 2 * 2 if w_dtype in ("i4", "u4") else 0
     assert c.q.ws_bytes == M * N * 4 + zr
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([rng.choice(M, 200, replace=False), [0, 255, 256, M - 1]]))

@@ -329,9 +329,13 @@ size_t split_pad_bytes(const qgemm_plan* p, int64_t M) {
 #ifndef QG_ZERO_FOLD
 #define QG_ZERO_FOLD 1
 #endif
+// Signed int4 with groups of whole superblocks folds its offset 8 the same way (one
+// group over K takes the column scale in the epilogue instead).
 bool zero_fold_format(const qgemm_plan* p) {
-  return QG_ZERO_FOLD && QG_BIG4 && p->L.fmt == FMT_U4 && p->L.zeros &&
-         scale_mode(p->L.fmt, p->group_size) == SC_BLOCK && p->L.Kpad / 32 <= ROWSUM_MAX_UNITS;
+  const bool u4z = p->L.fmt == FMT_U4 && p->L.zeros;
+  const bool i4s = p->L.fmt == FMT_I4 && p->group_size > 0;
+  return QG_ZERO_FOLD && QG_BIG4 && (u4z || i4s) && scale_mode(p->L.fmt, p->group_size) == SC_BLOCK &&
+         p->L.Kpad / 32 <= ROWSUM_MAX_UNITS;
 }
 bool zero_fold(const qgemm_plan* p, const qg_choice& ch) {
   return zero_fold_format(p) && ch.path == QGEMM_PATH_MFMA && ch.dl_tile == DL_256x256;
@@ -347,6 +351,18 @@ size_t run_ws_bytes_for(const qgemm_plan* p, int64_t M, bool fold) {
 }
 // the workspace of a run of M rows with the kernels chosen for M
 size_t run_ws_bytes(const qgemm_plan* p, int64_t M, const qg_choice& ch) { return run_ws_bytes_for(p, M, zero_fold(p, ch)); }
+// The most rows of a run of this plan that takes the 256 x 256 tiles with the folding
+// (0: none).  The tile choice depends on the rows only through the number of 256-row
+// tiles (above 128 rows), so one run per tile count is checked, from the plan's down.
+int64_t fold_rows(const qgemm_plan* p) {
+  if (!zero_fold_format(p)) return 0;
+  for (int64_t rt = (p->M + 255) / 256; rt >= 1; --rt) {
+    const int64_t m = p->M < rt * 256 ? p->M : rt * 256;
+    if (m <= 128) break;
+    if (zero_fold(p, choose(p, m))) return m;
+  }
+  return 0;
+}
 
 // one run: the split-K fill, the kernel chosen for M rows, the finalize pass
 qgemm_status run_impl(const qgemm_plan* plan, int64_t M, const void* A, const void* packed, const void* bias,
@@ -515,10 +531,12 @@ qgemm_status qgemm_create(qgemm_plan** out, int64_t M, int64_t N, int64_t K, qge
   const size_t mn4 = (size_t)M * (size_t)N * 4;
   p->two_pass = k_parts > 1 && two_pass_split(M, mn4 * (size_t)k_parts, out_dtype == QGEMM_F16, flags);
   p->ch = choose(p, M);
-  // int32 output with atomics: none (straight into C).  With zero-point folding the
-  // row sums are counted whenever M could take the 256 x 256 tiles, so that runs of
-  // fewer rows never need more than the plan states
-  p->ws_bytes = run_ws_bytes_for(p, M, zero_fold_format(p) && (zero_fold(p, p->ch) || M > 128));
+  // int32 output with atomics: none (straight into C).  With the folding, the planes
+  // of the largest run that takes it, so that runs of fewer rows never need more than
+  // the plan states
+  p->ws_bytes = run_ws_bytes(p, M, p->ch);
+  const int64_t mf = fold_rows(p);
+  if (mf > 0 && run_ws_bytes_for(p, mf, true) > p->ws_bytes) p->ws_bytes = run_ws_bytes_for(p, mf, true);
   if (packed_bytes) *packed_bytes = p->L.total;
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
   *out = p;

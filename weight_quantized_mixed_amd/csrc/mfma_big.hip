@@ -86,14 +86,19 @@ struct BigGeo {
   static_assert(!PACKED || FMT == FMT_I2 || KB == 2 * SPOS, "an int4 superblock is two stages (two per iteration)");
 };
 
-template <int FMT, bool SCALED, bool ZEROS>
+// FOLD: a correction after the loop takes what the loop leaves of the weights' offset,
+// the zero points of uint4 (whose scale slot then holds (scale, zero) pairs) or the
+// offset 8 of signed int4; see nc below
+template <int FMT, bool SCALED, bool FOLD>
 __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
   using G = BigGeo<FMT, SCALED>;
   constexpr bool FP = G::FP, PACKED = G::PACKED;
   constexpr bool I4 = FMT == FMT_I4 || FMT == FMT_U4;
-  // scaled uint4: the upcast and scale fold into one packed fma (needs -1024 s, or with
-  // zero points -fp16(1024 + z) s, finite in fp16: |s| < 64, |s (1024 + z)| < 65504)
-  constexpr bool U4S = FMT == FMT_U4 && SCALED;
+  // scaled uint4, and folded signed int4: the upcast and scale fold into one packed fma
+  // (its addend, -1024 s, -fp16(1024 + z) s or -1032 s, must be finite in fp16:
+  // |s| < 63, |s (1024 + z)| < 65504)
+  constexpr bool U4S = SCALED && (FMT == FMT_U4 || (FMT == FMT_I4 && FOLD));
+  constexpr bool ZEROS = FOLD && FMT == FMT_U4;  // (scale, zero) pairs in the scale slot
   constexpr int KB = G::KB, ESZ = G::ESZ, ROWB = G::ROWB, SPOS = G::SPOS, BSB = G::BSB;
   constexpr int A_BYTES = G::A_BYTES, B_BYTES = G::B_BYTES, STAGE = G::STAGE, NSTAGE = G::NSTAGE;
   constexpr int LA = G::LA, LB = G::LB, L = G::L;
@@ -243,8 +248,8 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
         f.b[j] = *reinterpret_cast<const uint4*>(lb + t * 1024 + lane * 16);  // superblock t, piece = lane
       if constexpr (SCALED && t == 0 && scl) {
         const int col = (wn * 8 + j) * 16 + l16;
-        // with zero points the slot holds (scale, zero) pairs; the zero points are
-        // applied after the loop
+        // with zero points the slot holds (scale, zero) pairs; the zero points (and
+        // the offset of folded signed int4) are applied after the loop
         const uint32_t u = ZEROS ? *reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES + col * 4)
                                  : *reinterpret_cast<const uint16_t*>(base + A_BYTES + B_BYTES + col * 2);
         sc[j] = __builtin_amdgcn_perm(u, u, 0x01000100u);  // low half in both halves
@@ -255,6 +260,10 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
           // -(z - r) s - d goes with the zero points after the loop
           const uint32_t b = as_u32(as_h2(__builtin_amdgcn_perm(u, u, 0x03020302u)) + as_h2(k_exp));
           nc[j] = as_u32(as_h2(b) * -as_h2(sc[j]));
+        } else if constexpr (FMT == FMT_I4 && U4S) {
+          // signed int4, stored q + 8: its offset as a zero point z = 8, b = 1032, c =
+          // fp16(-1032 s); -d goes after the loop
+          nc[j] = as_u32(as_h2(sc[j]) * as_h2(0xE408E408u));
         } else if constexpr (U4S) {
           nc[j] = as_u32(as_h2(sc[j]) * as_h2(0xE400E400u));  // -1024 s, exact
         }
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
 #undef QG_BIG_STAGE
     wait_vmcnt<0>();  // drain the tail copies before the workgroup's LDS is released
   }
-  if constexpr (ZEROS) {
+  if constexpr (FOLD) {
     // The zero points, applied after the loop: acc += sum over groups g of R[m, g]
     // P[g, n] with P = -(z - r) s - d (the part of the zero point and the rounding of
     // the fma's addend that the loop left, see nc; R: the rows of A summed over each
@@ -484,10 +493,10 @@ __global__ __launch_bounds__(256) void mfma_big_kernel(RunArgs a) {
   }
 }
 
-template <int FMT, bool SCALED, bool ZEROS>
+template <int FMT, bool SCALED, bool FOLD>
 hipError_t launch_big_t(const RunArgs& a, hipStream_t st) {
   const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  hipLaunchKernelGGL((mfma_big_kernel<FMT, SCALED, ZEROS>), dim3(tiles * a.k_parts), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((mfma_big_kernel<FMT, SCALED, FOLD>), dim3(tiles * a.k_parts), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -503,7 +512,9 @@ hipError_t launch_mfma_big(int fmt, const RunArgs& a, hipStream_t st) {
   const bool sc = a.smode != SC_NONE;
   switch (fmt) {
     case FMT_F16: return launch_big_t<FMT_F16, false, false>(a, st);
-    case FMT_I4: return sc ? launch_big_t<FMT_I4, true, false>(a, st) : launch_big_t<FMT_I4, false, false>(a, st);
+    case FMT_I4:
+      if (!sc) return launch_big_t<FMT_I4, false, false>(a, st);
+      return a.zr ? launch_big_t<FMT_I4, true, true>(a, st) : launch_big_t<FMT_I4, true, false>(a, st);
     case FMT_U4:
       if (a.zeros) return a.zr && sc ? launch_big_t<FMT_U4, true, true>(a, st) : hipErrorInvalidValue;
       return sc ? launch_big_t<FMT_U4, true, false>(a, st) : launch_big_t<FMT_U4, false, false>(a, st);

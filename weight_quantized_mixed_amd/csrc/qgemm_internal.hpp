@@ -112,12 +112,12 @@ struct RunArgs {
   // tiles: the per-column scale applied to the fp32 sum in the epilogue (the tiles
   // then upcast without it); null otherwise
   const _Float16* epi_scale;
-  // uint4 with zero points on the 256 x 256 tiles of four waves: the zero points are
-  // folded out of the K loop (C = sum_k A q s - sum_g R[m, g] s[g, n] z[g, n], R the
-  // row sums of A over scale group g).  zr holds R of each row, zp P = -s z of each
-  // column (Npad of them), each as two bf16 planes of zr_gp values, [hi | lo] with
-  // hi = bf16(x), lo = bf16(x - hi), groups zr_G .. zr_gp - 1 zero; both null when the
-  // zero points stay in the loop
+  // uint4 with zero points (and signed int4, its offset 8 as the zero point) on the
+  // 256 x 256 tiles of four waves: the zero points are folded out of the K loop
+  // (C = sum_k A q s - sum_g R[m, g] s[g, n] z[g, n], R the row sums of A over scale
+  // group g).  zr holds R of each row, zp the per-column term P of each column (Npad of
+  // them), each as two bf16 planes of zr_gp values, [hi | lo] with hi = bf16(x),
+  // lo = bf16(x - hi), groups zr_G .. zr_gp - 1 zero; both null without the folding
   const uint16_t* zr;
   const uint16_t* zp;
   int32_t zr_gp;  // groups per plane: zr_G rounded up to 32
@@ -190,8 +190,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // for the zero-point folding of the 256 x 256 tiles; a.K / 32 <= ROWSUM_MAX_UNITS
 constexpr int ROWSUM_MAX_UNITS = 8192;
 hipError_t launch_group_rowsum(const RunArgs& a, uint16_t* zr, hipStream_t st);
-// zp = the bf16 planes [P_hi | P_lo] of P = -s z for each of the Npad columns, from the
-// (scale, zero) pairs a.S ([zr_G][Npad])
+// zp = the bf16 planes [P_hi | P_lo] of the per-column term of the folding for each of
+// the Npad columns, from the (scale, zero) pairs a.S ([zr_G][Npad]), or for signed int4
+// (a.zeros 0) from its fp16 scales with the offset 8 as the zero point
 hipError_t launch_zero_planes(const RunArgs& a, uint16_t* zp, hipStream_t st);
 // dst[m, k] = k < K ? A[m, k] : 0 for rows of Kpad elements of esz bytes (Kpad * esz a
 // multiple of 16, dst 16-byte aligned; A any alignment of its element size)

@@ -133,15 +133,17 @@ __global__ __launch_bounds__(256) void group_rowsum_kernel(const uint4* __restri
 // (q - r) s + d rounded once, d = c + b s (exact in fp32, as is b s); the term is
 // P = -(z - r) s - d, so that adding sum_g R[m, g] P[g, n] leaves (q - z) s.
 // Consecutive threads take consecutive columns of one group, so the pairs are read
-// in order.
-__global__ void zero_planes_kernel(const uint32_t* __restrict__ S, uint16_t* __restrict__ zp, int Npad, int G,
-                                   int gp) {
+// in order.  Signed int4 (pairs false: fp16 scales [G][Npad]) takes its offset 8 as
+// the zero point: b = 1032, r = 8, P = -d.
+__global__ void zero_planes_kernel(const void* __restrict__ S, uint16_t* __restrict__ zp, int Npad, int G, int gp,
+                                   bool pairs) {
   const int64_t total = (int64_t)Npad * gp;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int g = (int)(i / Npad), col = (int)(i - (int64_t)g * Npad);
     float p = 0.f;
     if (g < G) {
-      const uint32_t u = S[(size_t)g * Npad + col];
+      const uint32_t u = pairs ? static_cast<const uint32_t*>(S)[(size_t)g * Npad + col]
+                               : static_cast<const uint16_t*>(S)[(size_t)g * Npad + col] | 0x48000000u;  // z = 8
       const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
       const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
       const float b = (float)(_Float16)(z + 1024.f);  // z + 1024 is exact in fp32
@@ -197,8 +199,8 @@ hipError_t launch_group_rowsum(const RunArgs& a, uint16_t* zr, hipStream_t st) {
 
 hipError_t launch_zero_planes(const RunArgs& a, uint16_t* zp, hipStream_t st) {
   if (!a.S || a.zr_gp % 32 != 0 || a.zr_G > a.zr_gp) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(zero_planes_kernel, dim3(grid_for((size_t)a.Npad * a.zr_gp, 256)), dim3(256), 0, st,
-                     static_cast<const uint32_t*>(a.S), zp, a.Npad, a.zr_G, a.zr_gp);
+  hipLaunchKernelGGL(zero_planes_kernel, dim3(grid_for((size_t)a.Npad * a.zr_gp, 256)), dim3(256), 0, st, a.S, zp,
+                     a.Npad, a.zr_G, a.zr_gp, a.zeros != 0);
   return hipGetLastError();
 }
 
