@@ -91,7 +91,7 @@ __device__ __forceinline__ float sum8_f16(uint4 v) {
 // butterfly, so every run rounds alike, and after a barrier lane g adds the units of
 // group g in order.  Row length K (a multiple of 32, at most 32 * ROWSUM_MAX_UNITS);
 // units: K / 32 floats of dynamic LDS.
-constexpr int ROWSUM_BATCH = 4;  // chunks per lane in flight
+constexpr int ROWSUM_BATCH = 8;  // chunks per lane in flight
 __global__ __launch_bounds__(256) void group_rowsum_kernel(const uint4* __restrict__ A, uint16_t* __restrict__ zr,
                                                            int K, int upg, int G, int gp) {
   extern __shared__ float unit[];
@@ -137,24 +137,39 @@ __global__ __launch_bounds__(256) void group_rowsum_kernel(const uint4* __restri
 // the zero point: b = 1032, r = 8, P = -d.
 __global__ void zero_planes_kernel(const void* __restrict__ S, uint16_t* __restrict__ zp, int Npad, int G, int gp,
                                    bool pairs) {
-  const int64_t total = (int64_t)Npad * gp;
+  // a thread takes 8 consecutive groups of one column (16 bytes of each plane); the
+  // threads of a run take consecutive columns, so each group's reads stay in order
+  const int64_t total = (int64_t)Npad * (gp / 8);
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int g = (int)(i / Npad), col = (int)(i - (int64_t)g * Npad);
-    float p = 0.f;
-    if (g < G) {
-      const uint32_t u = pairs ? static_cast<const uint32_t*>(S)[(size_t)g * Npad + col]
-                               : static_cast<const uint16_t*>(S)[(size_t)g * Npad + col] | 0x48000000u;  // z = 8
-      const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
-      const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
-      const float b = (float)(_Float16)(z + 1024.f);  // z + 1024 is exact in fp32
-      const float bs = b * s;                         // exact: 11 x 11 significant bits
-      const float d = (float)(_Float16)(-bs) + bs;    // the rounding of c, exact
-      p = -(z - (b - 1024.f)) * s - d;
+    const int gb = (int)(i / Npad), col = (int)(i - (int64_t)gb * Npad);
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int g = gb * 8 + e;
+      float p = 0.f;
+      if (g < G) {
+        const uint32_t u = pairs ? static_cast<const uint32_t*>(S)[(size_t)g * Npad + col]
+                                 : static_cast<const uint16_t*>(S)[(size_t)g * Npad + col] | 0x48000000u;  // z = 8
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+        const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+        const float b = (float)(_Float16)(z + 1024.f);  // z + 1024 is exact in fp32
+        const float bs = b * s;                         // exact: 11 x 11 significant bits
+        const float d = (float)(_Float16)(-bs) + bs;    // the rounding of c, exact
+        p = -(z - (b - 1024.f)) * s - d;
+      }
+      const uint32_t h = bf16_rne(p);
+      const uint32_t l = bf16_rne(p - __uint_as_float(h << 16));
+      if (e & 1) {
+        hi[e / 2] |= h << 16;
+        lo[e / 2] |= l << 16;
+      } else {
+        hi[e / 2] = h;
+        lo[e / 2] = l;
+      }
     }
-    const uint16_t hi = bf16_rne(p);
-    uint16_t* o = zp + (size_t)col * 2 * gp + g;
-    o[0] = hi;
-    o[gp] = bf16_rne(p - __uint_as_float((uint32_t)hi << 16));
+    uint4* o = reinterpret_cast<uint4*>(zp + (size_t)col * 2 * gp + gb * 8);  // 16-byte aligned: gp % 32 == 0
+    o[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    o[gp / 8] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
 }
 
@@ -199,7 +214,7 @@ hipError_t launch_group_rowsum(const RunArgs& a, uint16_t* zr, hipStream_t st) {
 
 hipError_t launch_zero_planes(const RunArgs& a, uint16_t* zp, hipStream_t st) {
   if (!a.S || a.zr_gp % 32 != 0 || a.zr_G > a.zr_gp) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(zero_planes_kernel, dim3(grid_for((size_t)a.Npad * a.zr_gp, 256)), dim3(256), 0, st, a.S, zp,
+  hipLaunchKernelGGL(zero_planes_kernel, dim3(grid_for((size_t)a.Npad * (a.zr_gp / 8), 256)), dim3(256), 0, st, a.S, zp,
                      a.Npad, a.zr_G, a.zr_gp, a.zeros != 0);
   return hipGetLastError();
 }
